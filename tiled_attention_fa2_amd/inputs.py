@@ -1,0 +1,104 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module only draws random numbers and shapes them. It holds none of the
+attention or quantisation arithmetic, so the CPU oracle and the HIP path can
+both be fed from it without sharing any of the method.
+
+Workloads follow the shapes the pages measure on: the MiniMax H3 DiT block's
+self-attention (56 heads x 30272 tokens x head dim 128) from "1.8x Faster
+Attention on an RTX 5080", section "The attention itself", plus the small and
+causal shapes used for parity. The real activations are not available; iid
+N(0, 1) tensors of the same shapes stand in for them.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32", "bf16" or "fp8" (fp8 = bf16 draws quantised per head)
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self) -> float:
+        """4*B*H*N^2*d, halved for causal (the pages' accounting)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("f32_b1_h1_n256_d64", "f32", 1, 1, 256, 64, False),
+        Workload("bf16_b1_h8_n4096_d128", "bf16", 1, 8, 4096, 128, False),
+        Workload("bf16_causal_b4_h32_n2048_d128", "bf16", 4, 32, 2048, 128, True),
+        Workload("bf16_dit_b1_h56_n30272_d128", "bf16", 1, 56, 30272, 128, False),
+        Workload("fp8_dit_b1_h56_n30272_d128", "fp8", 1, 56, 30272, 128, False),
+    )
+}
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
+             variant: str = "iid"):
+    """Draw Q, then K, then V as iid N(0,1) float32 on the CPU with one seeded
+    generator, then round to bf16 unless dtype == "f32".
+
+    variant shapes the draws for stress cases (all still seeded):
+      "iid"      plain N(0,1)
+      "peaked"   Q multiplied by 8: near one-hot rows, frequent rescales
+      "growing"  key norms rise along the sequence, so the running max rises
+                 on almost every key tile
+      "outlier"  a few channels of Q, K and V multiplied by 20 (the kind of
+                 outliers that make fp8 hard)
+    """
+    g = torch.Generator().manual_seed(seed)
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if variant == "peaked":
+        q = q * 8.0
+    elif variant == "growing":
+        ramp = torch.linspace(0.25, 3.0, N, dtype=torch.float32).view(1, 1, N, 1)
+        k = k * ramp
+    elif variant == "outlier":
+        ch = torch.randperm(d, generator=g)[: max(1, d // 32)]
+        for t in (q, k, v):
+            t[..., ch] *= 20.0
+    elif variant != "iid":
+        raise ValueError(f"unknown variant {variant!r}")
+    if dtype == "f32":
+        return q, k, v
+    if dtype in ("bf16", "fp8"):
+        return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_workload(name: str, seed: int = 0, variant: str = "iid"):
+    w = WORKLOADS[name]
+    return w, make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed, variant=variant)
+
+
+def sample_rows(N: int, tile: int = 128, n_random: int = 64, seed: int = 12345):
+    """Query rows checked at full size: rows 0, 1, N-1, every row of the last
+    (ragged) query tile and n_random uniform draws, sorted and unique."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    last_tile_start = ((N - 1) // tile) * tile
+    rows = {0, 1, N - 1}
+    rows.update(range(last_tile_start, N))
+    rows.update(int(r) for r in rng.integers(0, N, size=n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < N), dtype=np.int64)
