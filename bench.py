@@ -1,0 +1,197 @@
+"""Benchmark of the FlashAttention-2 forward on one MI355X.
+
+Default workload: the MiniMax H3 DiT self-attention shape the pages measure
+("1.8x Faster Attention on an RTX 5080", section "The attention itself"):
+B=1, H=56, N=30272, d=128, non-causal, bf16, with iid N(0,1) synthetic inputs
+in place of the model's activations. The same shape in FP8-e4m3 (per-head
+quantised from the same bf16 draws) is timed next to it.
+
+A step is one fa_fwd over the whole batch with inputs resident in HBM.
+FLOP per step = 4*B*H*N^2*d (halved for causal), the pages' accounting.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak (bf16 / fp8), H=56 N=30272 d=128"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense MFMA
+KERNEL_SOURCES = ["tiled_attention_fa2_amd/csrc/fa_fwd_kernel.hpp",
+                  "tiled_attention_fa2_amd/csrc/fa_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only if
+    it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_fwd(fa, torch, args_in, kw, steps, warmup):
+    """Warm up, then time exactly `steps` launches. Returns (region ms per
+    step, mean kernel ms from per-launch events)."""
+    o, lse = fa.fwd(*args_in, **kw)
+    kw = dict(kw, out=o, lse=lse)
+    for _ in range(warmup):
+        fa.fwd(*args_in, **kw)
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fa.fwd(*args_in, **kw)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    region_ms = starts[0].elapsed_time(ends[-1]) / steps
+    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return max(region_ms, 1e-9), kern_ms, wall_ms
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the fp64 oracle on a bounded sample of the same workload: chunks of
+    128 query rows against all N keys, cycling over heads, until budget_s."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    qn = q.float().numpy()
+    kn = k.float().numpy()
+    vn = v.float().numpy()
+    rows_done = 0
+    t0 = time.perf_counter()
+    h = 0
+    r0 = 0
+    while time.perf_counter() - t0 < budget_s:
+        rows = np.arange(r0, min(r0 + 128, w.N))
+        oracle.attention(qn[:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], w.scale,
+                         causal=w.causal, rows=rows)
+        rows_done += len(rows)
+        h = (h + 1) % w.H
+        r0 = (r0 + 128) % w.N
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.d * w.N * rows_done      # non-causal: every row sees N keys
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows_done} query rows x all {w.N} keys (chunks of 128 rows, cycling heads) "
+                      f"of {w.name}, fp64 numpy, {dt:.1f} s",
+            "extrapolated_full_problem_s": dt * (w.B * w.H * w.N) / rows_done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_dit_b1_h56_n30272_d128")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the forward shards by head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tiled_attention_fa2_amd import fa
+    from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, "f32" if w.dtype == "f32" else "bf16", seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+
+    if w.dtype == "fp8":
+        q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
+        main_in, main_kw = (q8, k8, v8), dict(causal=w.causal, scale=w.scale, descales=ds)
+    else:
+        main_in, main_kw = (qd, kd, vd), dict(causal=w.causal, scale=w.scale)
+    print("[bench] timing main leg", file=sys.stderr, flush=True)
+    ms, kern_ms, wall_ms = time_fwd(fa, torch, main_in, main_kw, a.steps, a.warmup)
+    flops = w.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "pct_of_mfma_peak": round(100 * value / peak, 2),
+                   "wall_ms_per_step": round(wall_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "fa_fwd_kernel", "kernel_ms": round(kern_ms, 4)},
+    }
+
+    if not a.no_fp8 and w.dtype == "bf16" and w.name.startswith("bf16_dit"):
+        w8 = WORKLOADS["fp8_dit_b1_h56_n30272_d128"]
+        print("[bench] timing fp8 leg", file=sys.stderr, flush=True)
+        q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
+        ms8, kern8, _ = time_fwd(fa, torch, (q8, k8, v8),
+                                 dict(causal=False, scale=w8.scale, descales=ds), a.steps, a.warmup)
+        # per-head quantise of Q, K and V (the FP8 path's first step), timed on its own
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            fa.quantize_qkv_fp8(qd, kd, vd)
+        e1.record()
+        torch.cuda.synchronize()
+        qms = e0.elapsed_time(e1) / a.steps
+        v8 = w8.flops() / (ms8 * 1e-3) / 1e12
+        out["fp8"] = {
+            "workload": w8.name, "value": round(v8, 2), "unit": "TFLOP/s", "ms_per_step": round(ms8, 4),
+            "pct_of_mfma_peak": round(100 * v8 / PEAK_TFLOPS["fp8"], 2),
+            "quantize_qkv_ms": round(qms, 4),
+            "value_incl_quantize": round(w8.flops() / ((ms8 + qms) * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(w8.flops() / (kern8 * 1e-3) / 1e12, 2),
+                         "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                         "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                         "traffic": measured_traffic(w8.name), "kernel": "fa_fwd_kernel",
+                         "kernel_ms": round(kern8, 4)},
+        }
+
+    if a.cpu_budget > 0:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

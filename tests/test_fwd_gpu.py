@@ -1,0 +1,203 @@
+"""Parity of the HIP forward (through the C ABI) with the fp64 CPU oracle.
+
+Tolerances (max-abs over the compared elements):
+  O: 1e-5 (fp32), 1e-2 (bf16), 6e-2 (fp8, plus cosine >= 0.999 with the
+  oracle fed the same fp8 inputs); L: 1e-3 for every dtype.
+The three small workloads are compared on every row; the two 56-head x 30272
+workloads, in the launch configuration the benchmark times, on a seeded
+sample of rows (0, 1, N-1, the ragged last query tile, 64 random rows).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tiled_attention_fa2_amd import fa
+from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-5, "bf16": 1e-2, "fp8": 6e-2}
+TOL_L = 1e-3
+
+
+def _dev(*ts):
+    return [t.cuda().contiguous() for t in ts]
+
+
+def _metrics(o_gpu, O_ref):
+    a = o_gpu.astype(np.float64).ravel()
+    b = O_ref.ravel()
+    err = np.abs(a - b)
+    cos = float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+    rrms = float(np.sqrt(np.mean((a - b) ** 2)) / (np.sqrt(np.mean(b ** 2)) + 1e-300))
+    floor = float(np.max(np.abs(torch.from_numpy(b).to(torch.bfloat16).double().numpy() - b)))
+    return float(err.max()), cos, rrms, floor
+
+
+def _run(q, k, v, dtype, causal, scale):
+    """GPU forward; returns (O, L) on the host as float64 numpy, plus the fp64
+    inputs the oracle must see."""
+    if dtype == "fp8":
+        c_q, ds_q = oracle.quantize_per_head(q)
+        c_k, ds_k = oracle.quantize_per_head(k)
+        c_v, ds_v = oracle.quantize_per_head(v)
+        descales = torch.from_numpy(np.stack([ds_q.ravel(), ds_k.ravel(), ds_v.ravel()])).cuda()
+        qd, kd, vd = _dev(torch.from_numpy(c_q), torch.from_numpy(c_k), torch.from_numpy(c_v))
+        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, descales=descales)
+        ref_in = (oracle.dequantize_per_head(c_q, ds_q), oracle.dequantize_per_head(c_k, ds_k),
+                  oracle.dequantize_per_head(c_v, ds_v))
+    else:
+        qd, kd, vd = _dev(q, k, v)
+        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+        ref_in = (q, k, v)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ref_in
+
+
+def _check(q, k, v, dtype, causal, scale, rows=None, label=""):
+    print(f"[case] {label} dtype={dtype} shape={tuple(q.shape)} causal={causal} scale={scale}", flush=True)
+    O_gpu, L_gpu, ref_in = _run(q, k, v, dtype, causal, scale)
+    O_ref, L_ref = oracle.attention(*ref_in, scale=scale, causal=causal, rows=rows)
+    if rows is not None:
+        O_gpu = O_gpu[:, :, rows]
+        L_gpu = L_gpu[:, :, rows]
+    err_o, cos, rrms, floor = _metrics(O_gpu, O_ref)
+    err_l = float(np.max(np.abs(L_gpu - L_ref)))
+    print(f"    max|dO|={err_o:.3e} max|dL|={err_l:.3e} cos={cos:.6f} relRMS={rrms:.3e} "
+          f"bf16-floor={floor:.3e}", flush=True)
+    assert np.all(np.isfinite(O_gpu)) and np.all(np.isfinite(L_gpu))
+    assert err_o <= TOL_O[dtype], (label, err_o)
+    assert err_l <= TOL_L, (label, err_l)
+    if dtype == "fp8":
+        assert cos >= 0.999, (label, cos)
+    return err_o, err_l, cos
+
+
+# ---------------------------------------------------------------- workloads
+SMALL = ["f32_b1_h1_n256_d64", "bf16_b1_h8_n4096_d128", "bf16_causal_b4_h32_n2048_d128"]
+LARGE = ["bf16_dit_b1_h56_n30272_d128", "fp8_dit_b1_h56_n30272_d128"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_all_rows(name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+    _check(q, k, v, w.dtype, w.causal, w.scale, label=name)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_workload_sampled_rows(name):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+    rows = sample_rows(w.N, tile=128, n_random=64)
+    _check(q, k, v, w.dtype, w.causal, w.scale, rows=rows, label=name)
+
+
+# ---------------------------------------------------------- ragged / edge
+RAGGED_N = [1, 2, 5, 37, 100, 129, 200, 255]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(dtype, d, causal):
+    for N in RAGGED_N:
+        q, k, v = make_qkv(2, 3, N, d, dtype, seed=N)
+        _check(q, k, v, dtype, causal, 1.0 / math.sqrt(d), label=f"ragged N={N} d={d}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_multi_tile_ragged_causal(dtype):
+    # several query and key tiles, with a ragged tail on both
+    q, k, v = make_qkv(1, 2, 1000, 128, dtype, seed=7)
+    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label="N=1000 causal")
+    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label="N=1000")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scale_values(scale, dtype):
+    q, k, v = make_qkv(1, 2, 300, 64, dtype, seed=9)
+    for causal in (False, True):
+        _check(q, k, v, dtype, causal, scale, label=f"scale={scale}")
+
+
+@pytest.mark.parametrize("variant", ["peaked", "growing", "outlier"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_stress_inputs(variant, dtype):
+    q, k, v = make_qkv(1, 4, 2048, 128, dtype, seed=3, variant=variant)
+    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label=f"stress {variant}")
+    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label=f"stress {variant} causal")
+
+
+# ----------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_key_value_permutation_invariance(dtype):
+    q, k, v = make_qkv(1, 2, 777, 128, dtype, seed=5)
+    perm = torch.randperm(777, generator=torch.Generator().manual_seed(1))
+    qd, kd, vd = _dev(q, k, v)
+    o1, l1 = fa.fwd(qd, kd, vd)
+    o2, l2 = fa.fwd(qd, kd[:, :, perm].contiguous(), vd[:, :, perm].contiguous())
+    torch.cuda.synchronize()
+    tol = 2 * TOL_O[dtype]
+    assert (o1.float() - o2.float()).abs().max().item() <= tol
+    assert (l1 - l2).abs().max().item() <= TOL_L
+
+
+def test_deterministic_bitwise():
+    for dtype, causal in (("bf16", False), ("bf16", True), ("f32", False), ("fp8", False)):
+        q, k, v = make_qkv(2, 4, 1500, 128, dtype, seed=2)
+        if dtype == "fp8":
+            qd, kd, vd = _dev(q, k, v)
+            q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
+            args, kw = (q8, k8, v8), dict(descales=ds)
+        else:
+            args, kw = tuple(_dev(q, k, v)), {}
+        o1, l1 = fa.fwd(*args, causal=causal, **kw)
+        o2, l2 = fa.fwd(*args, causal=causal, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (dtype, causal)
+
+
+# ------------------------------------------------------------- fp8 quantiser
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_quantiser_byte_exact(src):
+    q, _, _ = make_qkv(2, 5, 1234, 128, "f32" if src == "f32" else "bf16", seed=4)
+    q[1, 2] = 0.0                                   # an all-zero head
+    q[0, 3, 7, 5] = 1e-30 if src == "f32" else 0.0
+    codes_ref, ds_ref = oracle.quantize_per_head(q)
+    codes, ds = fa.quantize_fp8(q.cuda().contiguous())
+    torch.cuda.synchronize()
+    assert np.array_equal(ds.cpu().numpy().reshape(ds_ref.shape), ds_ref)
+    got = codes.cpu().numpy()
+    mism = int(np.sum(got != codes_ref))
+    assert mism == 0, f"{mism} code mismatches"
+
+
+def test_quantise_then_forward_end_to_end():
+    w = WORKLOADS["fp8_dit_b1_h56_n30272_d128"]
+    q, k, v = make_qkv(1, 8, 4096, 128, "bf16", seed=0)
+    qd, kd, vd = _dev(q, k, v)
+    q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
+    o, lse = fa.fwd(q8, k8, v8, descales=ds)
+    torch.cuda.synchronize()
+    refs = [oracle.quantize_per_head(t) for t in (q, k, v)]
+    ref_in = [oracle.dequantize_per_head(c, s) for c, s in refs]
+    O_ref, L_ref = oracle.attention(*ref_in, scale=w.scale)
+    err_o, cos, _, _ = _metrics(o.float().cpu().double().numpy(), O_ref)
+    assert err_o <= TOL_O["fp8"] and cos >= 0.999
+    assert np.max(np.abs(lse.cpu().double().numpy() - L_ref)) <= TOL_L
+
+
+# ---------------------------------------------------------------- error paths
+def test_binding_rejects_bad_arguments_on_device():
+    q, k, v = _dev(*make_qkv(1, 1, 64, 96, "bf16"))
+    with pytest.raises(fa.FAError) as e:
+        fa.fwd(q, k, v)
+    assert e.value.status == -4
+    q8 = torch.zeros((1, 1, 64, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd(q8, q8, q8)

@@ -1,0 +1,42 @@
+"""Builds libfa.so (the HIP kernels and the C ABI of include/fa.h) in-tree for
+gfx950 with hipcc. Run as `python -m tiled_attention_fa2_amd.build`."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = [os.path.join(PKG, "csrc", "fa_api.hip")]
+HEADERS = [os.path.join(ROOT, "include", "fa.h"),
+           os.path.join(PKG, "csrc", "fa_fwd_kernel.hpp"),
+           os.path.join(PKG, "csrc", "fa_quant_kernel.hpp")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU forms stay off: ordinary float code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(PKG, "csrc"),
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libfa.so")
+    if verbose and r.stderr.strip():
+        sys.stderr.write(r.stderr)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,119 @@
+// Per-head FP8-e4m3 quantisation for gfx950.
+//
+// "1.8x Faster Attention on an RTX 5080" (section "Who am I, what's mine?")
+// feeds its kernel FP8 Q, K and V with one fp32 descale per head. Per
+// (batch, head): amax = max |x|; descale = amax / 448; code =
+// e4m3(clamp(x * 448 / amax, -448, 448)), rounded to nearest even. An all-zero
+// head gets descale 1.
+//
+// The work is HBM-bound (read 2 or 4 bytes, write 1 byte per element), so the
+// kernels are plain streaming loops: 16 elements per thread per step with
+// 16-byte vector loads and stores, many workgroups per head, and the per-head
+// amax combined with one atomic max per workgroup on the float's bit pattern
+// (non-negative floats order like their unsigned bit patterns).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef unsigned int qu32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void fa_amax_clear(uint32_t* amax_bits, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) amax_bits[i] = 0u;
+}
+
+// Load 16 consecutive elements starting at element `e` as floats.
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* base, size_t e, float* out) {
+  if constexpr (BF16) {
+    const qu32x4* src = (const qu32x4*)((const unsigned short*)base + e);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const qu32x4 w = src[h];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        out[8 * h + 2 * k] = __builtin_bit_cast(float, w[k] << 16);
+        out[8 * h + 2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+      }
+    }
+  } else {
+    const qu32x4* src = (const qu32x4*)((const float*)base + e);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const qu32x4 w = src[h];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) out[4 * h + k] = __builtin_bit_cast(float, w[k]);
+    }
+  }
+}
+
+// grid = (blocks per head, B*H); per_head = N*d elements, a multiple of 16.
+template <bool BF16>
+__global__ void __launch_bounds__(256) fa_amax_kernel(const void* x, uint32_t* amax_bits,
+                                                      long long per_head) {
+  const int bh = blockIdx.y;
+  const size_t head0 = (size_t)bh * (size_t)per_head;
+  const long long n16 = per_head / 16;
+  float m = 0.0f;
+  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < n16;
+       t += (long long)gridDim.x * blockDim.x) {
+    float v[16];
+    load16<BF16>(x, head0 + (size_t)t * 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  // wave reduction, then one value per wave through LDS
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(amax_bits + bh, __builtin_bit_cast(uint32_t, b));
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) fa_quant_kernel(const void* x, uint8_t* out,
+                                                       const uint32_t* amax_bits,
+                                                       long long per_head) {
+  const int bh = blockIdx.y;
+  const float amax = __builtin_bit_cast(float, amax_bits[bh]);
+  // correctly rounded fp32 division (no fast-math anywhere in this library)
+  const float mult = amax == 0.0f ? 1.0f : 448.0f / amax;
+  const size_t head0 = (size_t)bh * (size_t)per_head;
+  const long long n16 = per_head / 16;
+  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < n16;
+       t += (long long)gridDim.x * blockDim.x) {
+    float v[16];
+    load16<BF16>(x, head0 + (size_t)t * 16, v);
+    qu32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = fminf(fmaxf(v[4 * w + k] * mult, -448.0f), 448.0f);
+      int pk = 0;
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], pk, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+      o[w] = (uint32_t)pk;
+    }
+    *(qu32x4*)(out + head0 + (size_t)t * 16) = o;
+  }
+}
+
+// amax (bit pattern, in place) -> descale = amax / 448, or 1 for amax == 0
+__global__ void fa_descale_finalize(uint32_t* amax_bits_then_descale, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float amax = __builtin_bit_cast(float, amax_bits_then_descale[i]);
+    const float ds = amax == 0.0f ? 1.0f : amax / 448.0f;
+    amax_bits_then_descale[i] = __builtin_bit_cast(uint32_t, ds);
+  }
+}
+
+}  // namespace fa

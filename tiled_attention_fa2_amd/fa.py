@@ -1,0 +1,154 @@
+"""Python binding of libfa.so (argument marshalling only).
+
+Every step of the attention forward and of the FP8 quantiser runs in the HIP
+kernels behind the C ABI of include/fa.h. This module only checks tensor
+metadata, allocates outputs with torch, and passes raw device pointers plus
+torch's current HIP stream. There is no fallback: if libfa.so is missing or a
+call fails, it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+# values of fa_dtype_t and fa_status_t in include/fa.h
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+FA_OK = 0
+STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
+          -4: "FA_ERR_HEAD_DIM", -5: "FA_ERR_SCALE", -6: "FA_ERR_DESCALES",
+          -7: "FA_ERR_ALIGN", -8: "FA_ERR_HIP"}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m tiled_attention_fa2_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
+        L.fa_fwd.restype = i
+        L.fa_quantize_fp8.argtypes = [vp, i, vp, vp, i, i, i, i, vp]
+        L.fa_quantize_fp8.restype = i
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DTYPE_FP8_E4M3
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share a dtype")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None,
+        out=None, lse=None):
+    """FlashAttention-2 forward. q, k, v: contiguous [B, H, N, d] device
+    tensors, all float32, all bfloat16, or all FP8 codes (uint8 or
+    float8_e4m3fn) with descales [3, B*H] float32. Returns (o, lse):
+    o [B, H, N, d] (float32 for float32 inputs, bfloat16 otherwise) and
+    lse [B, H, N] float32."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = torch.float32 if code == DTYPE_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.dtype != odt or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype, shape or layout")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if code == DTYPE_FP8_E4M3:
+        if descales is None:
+            raise ValueError("FP8 inputs need descales [3, B*H]")
+        if descales.dtype != torch.float32 or descales.numel() != 3 * B * H \
+                or not descales.is_contiguous() or not descales.is_cuda:
+            raise ValueError("descales must be a contiguous float32 device tensor of 3*B*H values")
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                      1 if causal else 0, float(scale), code,
+                      _ptr(descales) if code == DTYPE_FP8_E4M3 else None, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return out, lse
+
+
+def quantize_fp8(x, out=None, descale=None):
+    """Per-head e4m3 quantisation of a contiguous [B, H, N, d] float32 or
+    bfloat16 device tensor. Returns (codes uint8 [B, H, N, d],
+    descale float32 [B*H])."""
+    if not x.is_cuda or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] device tensor")
+    B, H, N, d = x.shape
+    if x.dtype == torch.bfloat16:
+        code = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        code = DTYPE_F32
+    else:
+        raise TypeError("quantize_fp8 takes float32 or bfloat16")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
+    st = lib().fa_quantize_fp8(_ptr(x), code, _ptr(out), _ptr(descale), B, H, N, d, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_fp8")
+    return out, descale
+
+
+def quantize_qkv_fp8(q, k, v):
+    """Quantise Q, K and V per head. Returns (q8, k8, v8, descales [3, B*H])."""
+    B, H = q.shape[:2]
+    descales = torch.empty((3, B * H), dtype=torch.float32, device=q.device)
+    q8, _ = quantize_fp8(q, descale=descales[0])
+    k8, _ = quantize_fp8(k, descale=descales[1])
+    v8, _ = quantize_fp8(v, descale=descales[2])
+    return q8, k8, v8, descales
