@@ -3,6 +3,11 @@
 Tolerances (max-abs over the compared elements):
   O: 1e-5 (fp32), 1e-2 (bf16), 6e-2 (fp8, plus cosine >= 0.999 with the
   oracle fed the same fp8 inputs); L: 1e-3 for every dtype.
+These are applied as they stand to the five named workloads. The other cases
+(ragged lengths, causal rows with a handful of keys, stress inputs with large
+|O|) add to the O tolerance the bf16 rounding floor of the exact answer,
+max |bf16(O_ref) - O_ref|: the output format itself cannot do better, and for
+|O| >= 4 that floor alone exceeds 1e-2.
 The three small workloads are compared on every row; the two 56-head x 30272
 workloads, in the launch configuration the benchmark times, on a seeded
 sample of rows (0, 1, N-1, the ragged last query tile, 64 random rows).
@@ -57,7 +62,7 @@ def _run(q, k, v, dtype, causal, scale):
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ref_in
 
 
-def _check(q, k, v, dtype, causal, scale, rows=None, label=""):
+def _check(q, k, v, dtype, causal, scale, rows=None, label="", extra=True, bounds=None):
     print(f"[case] {label} dtype={dtype} shape={tuple(q.shape)} causal={causal} scale={scale}", flush=True)
     O_gpu, L_gpu, ref_in = _run(q, k, v, dtype, causal, scale)
     O_ref, L_ref = oracle.attention(*ref_in, scale=scale, causal=causal, rows=rows)
@@ -69,8 +74,13 @@ def _check(q, k, v, dtype, causal, scale, rows=None, label=""):
     print(f"    max|dO|={err_o:.3e} max|dL|={err_l:.3e} cos={cos:.6f} relRMS={rrms:.3e} "
           f"bf16-floor={floor:.3e}", flush=True)
     assert np.all(np.isfinite(O_gpu)) and np.all(np.isfinite(L_gpu))
-    assert err_o <= TOL_O[dtype], (label, err_o)
-    assert err_l <= TOL_L, (label, err_l)
+    tol_o = TOL_O[dtype] + (floor if extra and dtype != "f32" else 0.0)
+    tol_l = TOL_L
+    if bounds is not None:
+        tol_o, tol_l = bounds(ref_in, scale, floor)
+        print(f"    derived bounds: O {tol_o:.3e}  L {tol_l:.3e}", flush=True)
+    assert err_o <= tol_o, (label, err_o, tol_o)
+    assert err_l <= tol_l, (label, err_l, tol_l)
     if dtype == "fp8":
         assert cos >= 0.999, (label, cos)
     return err_o, err_l, cos
@@ -85,7 +95,7 @@ LARGE = ["bf16_dit_b1_h56_n30272_d128", "fp8_dit_b1_h56_n30272_d128"]
 def test_workload_all_rows(name):
     w = WORKLOADS[name]
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
-    _check(q, k, v, w.dtype, w.causal, w.scale, label=name)
+    _check(q, k, v, w.dtype, w.causal, w.scale, label=name, extra=False)
 
 
 @pytest.mark.parametrize("name", LARGE)
@@ -93,7 +103,7 @@ def test_workload_sampled_rows(name):
     w = WORKLOADS[name]
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
     rows = sample_rows(w.N, tile=128, n_random=64)
-    _check(q, k, v, w.dtype, w.causal, w.scale, rows=rows, label=name)
+    _check(q, k, v, w.dtype, w.causal, w.scale, rows=rows, label=name, extra=False)
 
 
 # ---------------------------------------------------------- ragged / edge
@@ -125,12 +135,34 @@ def test_scale_values(scale, dtype):
         _check(q, k, v, dtype, causal, scale, label=f"scale={scale}")
 
 
+def _fp8_outlier_bounds(ref_in, scale, floor):
+    """Worst-case bounds for FP8 inputs with a few x20 channels, derived from
+    the arithmetic rather than from the iid workloads:
+      L: each score carries the fp8 MFMA's product-sum error, at most
+         EPS_FP8_ACC * scale * sum_d |q_d k_d| (pinned by the MFMA probe test),
+         and L moves by at most the largest score error;
+      O: P * 256 is rounded to e4m3 (3 mantissa bits, relative error <= 2^-4),
+         which moves a convex combination of V rows by at most 2^-4 max|V|,
+         plus the score error's effect and the bf16 output floor."""
+    from test_mfma_layout_gpu import EPS_FP8_ACC
+
+    qd, kd, vd = ref_in
+    ds = 0.0
+    for b in range(qd.shape[0]):
+        for h in range(qd.shape[1]):
+            ds = max(ds, float(np.max(np.abs(qd[b, h]) @ np.abs(kd[b, h]).T)))
+    dS = EPS_FP8_ACC * abs(scale) * ds
+    vmax = float(np.max(np.abs(vd)))
+    return TOL_O["fp8"] + floor + 2.0 ** -4 * vmax + 2 * dS * vmax, TOL_L + dS
+
+
 @pytest.mark.parametrize("variant", ["peaked", "growing", "outlier"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_stress_inputs(variant, dtype):
     q, k, v = make_qkv(1, 4, 2048, 128, dtype, seed=3, variant=variant)
-    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label=f"stress {variant}")
-    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label=f"stress {variant} causal")
+    bounds = _fp8_outlier_bounds if (dtype == "fp8" and variant == "outlier") else None
+    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label=f"stress {variant}", bounds=bounds)
+    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label=f"stress {variant} causal", bounds=bounds)
 
 
 # ----------------------------------------------------------------- invariants

@@ -24,17 +24,31 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", LIB + ".tmp"]
+PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
+
+
+def _hipcc(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfa.so")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The one-wave MFMA layout/precision probe used by the GPU tests."""
+    _hipcc([HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_LIB + ".tmp"], verbose)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    _hipcc([HIPCC, *FLAGS, *extra, *SOURCES, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
+    if os.path.exists(PROBE_SRC):
+        build_probe(verbose)
     return LIB
 
 

@@ -61,6 +61,12 @@ template <> struct Traits<kF32>  { static constexpr int ES = 4; static constexpr
 template <> struct Traits<kBF16> { static constexpr int ES = 2; static constexpr int KPL = 8;  };
 template <> struct Traits<kFP8>  { static constexpr int ES = 1; static constexpr int KPL = 32; };
 
+// Reinterpretation of a 32-bit value. Taking the argument by value matters:
+// __builtin_bit_cast applied directly to an element of an ext_vector_type
+// value has been seen to read element 0 whatever the index.
+__host__ __device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__host__ __device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 template <int DT> struct Operand {
   static constexpr int DW = Traits<DT>::KPL * Traits<DT>::ES / 4;
   uint32_t w[DW];
@@ -77,8 +83,7 @@ __device__ __forceinline__ void mfma(const Operand<DT>& a, const Operand<DT>& b,
                                                         __builtin_bit_cast(i32x8, b), c,
                                                         0, 0, 0, 127, 0, 127);
   } else {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.w[0]),
-                                             __builtin_bit_cast(float, b.w[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(u2f(a.w[0]), u2f(b.w[0]), c, 0, 0, 0);
   }
 }
 
@@ -140,20 +145,30 @@ __host__ __device__ __forceinline__ constexpr int vt_pos(int key) {
   return n * 2 * KPL + hh * KPL + s;
 }
 
+// Exchange between the two 32-lane halves of a wave: on return, lane l holds
+// in (a, b) the entry values of lanes l%32 and l%32 + 32 (v_permlane32_swap
+// swaps the upper half of its first operand with the lower half of its
+// second). Written as inline asm with two distinct registers: the compiler
+// builtin, given the same value twice, has been seen to fold its two results
+// into one. The s_nop covers the VALU-write -> permlane-read wait states.
+// Must run with the whole wave active.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float swap_halves_max(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1]));
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float swap_halves_min(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, x), false, false);
-  return fminf(__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1]));
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fminf(a, b);
 }
 __device__ __forceinline__ float swap_halves_sum(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                            __builtin_bit_cast(unsigned, x), false, false);
-  return __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
 }
 
 // Block index -> logical work item. Workgroups are dispatched round-robin over
@@ -437,7 +452,7 @@ fa_fwd_kernel(FwdArgs p) {
           }
         } else {
           const int r0 = n;
-          pop[n].w[0] = __builtin_bit_cast(uint32_t, s[r0 >> 4][r0 & 15]);
+          pop[n].w[0] = f2u(s[r0 >> 4][r0 & 15]);
         }
       }
 

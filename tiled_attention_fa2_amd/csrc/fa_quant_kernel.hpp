@@ -20,6 +20,11 @@ namespace fa {
 
 typedef unsigned int qu32x4 __attribute__((ext_vector_type(4)));
 
+// 32-bit reinterpretations taking their argument by value (see f2u / u2f in
+// the forward kernel: bit-casting an ext_vector element in place is unsafe).
+__device__ __forceinline__ float q_u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t q_f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+
 __global__ void fa_amax_clear(uint32_t* amax_bits, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) amax_bits[i] = 0u;
@@ -35,8 +40,8 @@ __device__ __forceinline__ void load16(const void* base, size_t e, float* out) {
       const qu32x4 w = src[h];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        out[8 * h + 2 * k] = __builtin_bit_cast(float, w[k] << 16);
-        out[8 * h + 2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+        out[8 * h + 2 * k] = q_u2f(w[k] << 16);
+        out[8 * h + 2 * k + 1] = q_u2f(w[k] & 0xffff0000u);
       }
     }
   } else {
@@ -45,7 +50,7 @@ __device__ __forceinline__ void load16(const void* base, size_t e, float* out) {
     for (int h = 0; h < 4; ++h) {
       const qu32x4 w = src[h];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) out[4 * h + k] = __builtin_bit_cast(float, w[k]);
+      for (int k = 0; k < 4; ++k) out[4 * h + k] = q_u2f(w[k]);
     }
   }
 }
@@ -73,7 +78,7 @@ __global__ void __launch_bounds__(256) fa_amax_kernel(const void* x, uint32_t* a
   __syncthreads();
   if (threadIdx.x == 0) {
     const float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    atomicMax(amax_bits + bh, __builtin_bit_cast(uint32_t, b));
+    atomicMax(amax_bits + bh, q_f2u(b));
   }
 }
 
@@ -82,7 +87,7 @@ __global__ void __launch_bounds__(256) fa_quant_kernel(const void* x, uint8_t* o
                                                        const uint32_t* amax_bits,
                                                        long long per_head) {
   const int bh = blockIdx.y;
-  const float amax = __builtin_bit_cast(float, amax_bits[bh]);
+  const float amax = q_u2f(amax_bits[bh]);
   // correctly rounded fp32 division (no fast-math anywhere in this library)
   const float mult = amax == 0.0f ? 1.0f : 448.0f / amax;
   const size_t head0 = (size_t)bh * (size_t)per_head;
@@ -110,9 +115,9 @@ __global__ void __launch_bounds__(256) fa_quant_kernel(const void* x, uint8_t* o
 __global__ void fa_descale_finalize(uint32_t* amax_bits_then_descale, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) {
-    const float amax = __builtin_bit_cast(float, amax_bits_then_descale[i]);
+    const float amax = q_u2f(amax_bits_then_descale[i]);
     const float ds = amax == 0.0f ? 1.0f : amax / 448.0f;
-    amax_bits_then_descale[i] = __builtin_bit_cast(uint32_t, ds);
+    amax_bits_then_descale[i] = q_f2u(ds);
   }
 }
 
