@@ -11,8 +11,11 @@
 
 namespace {
 
-// Tile shapes: 4 waves x 32 query rows; key tile 64 (bf16), 128 (fp8), 32 (fp32).
+// Tile shapes: 4 waves x 32 query rows per workgroup; key tile 64 (bf16, fp8)
+// or 32 (fp32); registers bounded so two workgroups share a CU (2 waves per
+// SIMD): a single wave per SIMD cannot keep the MFMA pipe busy.
 constexpr int kWaves = 4;
+constexpr int kWavesPerSimd = 2;
 
 template <int DT, int D, int BN>
 int launch_fwd(const fa::FwdArgs& a, bool causal, hipStream_t stream) {
@@ -20,9 +23,9 @@ int launch_fwd(const fa::FwdArgs& a, bool causal, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)a.BH * a.n_qtiles));
   const dim3 block(C::NT);
   if (causal)
-    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, true, kWavesPerSimd>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, false, kWavesPerSimd>), grid, block, 0, stream, a);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -61,6 +64,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const int BM = 32 * kWaves;
   const long long n_qtiles = ((long long)N + BM - 1) / BM;
   if (BH > INT_MAX || BH * n_qtiles > INT_MAX) return FA_ERR_SHAPE;
+  // one head of Q, K or V is addressed with 32-bit buffer offsets
+  const long long es = dtype == FA_DTYPE_F32 ? 4 : dtype == FA_DTYPE_BF16 ? 2 : 1;
+  if (((long long)N + 128) * d * es > INT_MAX) return FA_ERR_SHAPE;
 
   fa::FwdArgs a;
   a.q = q;
@@ -80,8 +86,8 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
       return d == 128 ? launch_fwd<fa::kBF16, 128, 64>(a, c, stream)
                       : launch_fwd<fa::kBF16, 64, 64>(a, c, stream);
     case FA_DTYPE_FP8_E4M3:
-      return d == 128 ? launch_fwd<fa::kFP8, 128, 128>(a, c, stream)
-                      : launch_fwd<fa::kFP8, 64, 128>(a, c, stream);
+      return d == 128 ? launch_fwd<fa::kFP8, 128, 64>(a, c, stream)
+                      : launch_fwd<fa::kFP8, 64, 64>(a, c, stream);
     default:
       return d == 128 ? launch_fwd<fa::kF32, 128, 32>(a, c, stream)
                       : launch_fwd<fa::kF32, 64, 32>(a, c, stream);

@@ -112,15 +112,16 @@ struct Cfg {
   static constexpr int QK_STEPS = D / (2 * KPL);  // MFMAs per 32x32 score block
   static constexpr int PV_STEPS = BN / (2 * KPL); // k-steps of the PV product
   static constexpr int MB = D / 32;               // 32-row blocks of O^T
-  static constexpr int KROW = D * ES + 16;        // padded LDS row of K (bytes)
+  static constexpr int ROW = D * ES;              // bytes of one Q/K/V row in memory
+  static constexpr int KROW = ROW + 16;           // padded LDS row of K (bytes)
   static constexpr int VROW = BN * ES + 16;       // padded LDS row of V^T (bytes)
   static constexpr int KBYTES = BN * KROW;
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int KCHUNKS = BN * D * ES / 16;            // 16-byte chunks per K tile
-  static constexpr int KPT = (KCHUNKS + NT - 1) / NT;         // per thread
-  static constexpr int CPR = D * ES / 16;                     // 16-byte chunks per row
+  static constexpr int CPR = ROW / 16;                        // 16-byte chunks per row
+  static constexpr int KCHUNKS = BN * CPR;                    // 16-byte chunks per K tile
+  static constexpr int KPT = KCHUNKS / NT;                    // per thread
   static constexpr int EPC = 16 / ES;                         // elements per chunk
   static constexpr int VITEMS = (BN / 4) * CPR;               // (4-key group, chunk) items
   static constexpr int VPT = (VITEMS + NT - 1) / NT;
@@ -128,6 +129,7 @@ struct Cfg {
   static_assert(BN % (2 * KPL) == 0, "key tile must cover whole PV k-steps");
   static_assert(D % (2 * KPL) == 0 && D % 32 == 0, "head dim");
   static_assert(KCHUNKS % NT == 0, "K tile must split evenly over the threads");
+  static_assert(VITEMS % 64 == 0, "V items must fill whole waves");
 };
 
 // Position, inside one key tile of V^T in LDS, of key `key` (0 <= key < BN).
@@ -187,8 +189,32 @@ __host__ __device__ __forceinline__ void work_item(int bid, int total, int n_qti
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
-template <int DT, int D, int BN, int NWAVES, bool CAUSAL>
-__global__ void __launch_bounds__(64 * NWAVES)
+// Buffer resource over [base, base + bytes): loads at offsets >= bytes return
+// zero, which is how rows past the end of a head read as zeros without a
+// branch. 0x00020000 is the gfx9 raw-buffer word 3 (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value {hi, lo}
+// (selectors 0-3 pick bytes of lo, 4-7 bytes of hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> one dword of two bf16 (round to nearest even), low half first
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// WPE = waves per SIMD the register allocation must allow (1 or 2): with 2,
+// two workgroups share a CU and one wave's softmax overlaps another's MFMAs.
+template <int DT, int D, int BN, int NWAVES, bool CAUSAL, int WPE>
+__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_kernel(FwdArgs p) {
   using C = Cfg<DT, D, BN, NWAVES>;
   using Op = Operand<DT>;
@@ -209,32 +235,45 @@ fa_fwd_kernel(FwdArgs p) {
   const int q0w = q0 + 32 * wave;
   const int my_q = q0w + l32;
 
-  const size_t head_off = (size_t)bh * (size_t)N * D;  // elements
-  const unsigned char* Qg = (const unsigned char*)p.q + head_off * ES;
-  const unsigned char* Kg = (const unsigned char*)p.k + head_off * ES;
-  const unsigned char* Vg = (const unsigned char*)p.v + head_off * ES;
+  const uint32_t head_bytes = (uint32_t)N * C::ROW;   // < 2^31, checked by the host
+  const size_t head_off = (size_t)bh * head_bytes;
+  const unsigned char* Qg = (const unsigned char*)p.q + head_off;
+  const unsigned char* Kg = (const unsigned char*)p.k + head_off;
+  const unsigned char* Vg = (const unsigned char*)p.v + head_off;
 
   // scale * log2(e), with the fp8 descales of Q and K folded in
   float c = p.scale * 1.4426950408889634f;
-  float pv_scale = 1.0f;
+  float dv = 1.0f;
   if constexpr (DT == kFP8) {
     c *= p.descales[bh] * p.descales[p.BH + bh];
-    pv_scale = p.descales[2 * p.BH + bh] * (1.0f / 256.0f);
+    dv = p.descales[2 * p.BH + bh];
   }
+  // fp8 keeps P * 256 in e4m3's normal range ("1.8x Faster Attention on an
+  // RTX 5080", section "P goes through shared memory"): exp2(t + 8) = 256 exp2(t),
+  // folded into the subtraction of the running max at no cost.
+  constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
   const bool c_nonneg = c >= 0.0f;
   const float masked_raw = c_nonneg ? -__builtin_inff() : __builtin_inff();
 
   // ---- Q^T operands, held in registers for the whole loop ----
   Op qop[C::QK_STEPS];
   {
-    const bool qvalid = my_q < N;
-    const unsigned char* qrow = Qg + (size_t)(qvalid ? my_q : 0) * D * ES;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg, head_bytes);
+    // rows >= N start at or past head_bytes and read as zero
+    const uint32_t qoff = (uint32_t)my_q * C::ROW + hh * KPL * ES;
 #pragma unroll
     for (int kk = 0; kk < C::QK_STEPS; ++kk) {
-      const unsigned char* src = qrow + (size_t)(kk * 2 * KPL + hh * KPL) * ES;
+      const uint32_t off = qoff + kk * 2 * KPL * ES;
+      if constexpr (Op::DW >= 4) {
 #pragma unroll
-      for (int w = 0; w < Op::DW; ++w)
-        qop[kk].w[w] = qvalid ? ((const uint32_t*)src)[w] : 0u;
+        for (int x = 0; x < Op::DW / 4; ++x) {
+          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16 * x, 0, 0);
+#pragma unroll
+          for (int y = 0; y < 4; ++y) qop[kk].w[4 * x + y] = w[y];
+        }
+      } else {
+        qop[kk].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
+      }
     }
   }
 
@@ -245,78 +284,87 @@ fa_fwd_kernel(FwdArgs p) {
     n_ktiles = n_ktiles < last ? n_ktiles : last;
   }
 
-  // ---- staging registers for the next K / V tile ----
+  // ---- per-lane constant offsets ----
+  // K staging: chunk tid + it*NT of the tile -> row, 16-byte column
+  const int k_row0 = tid / C::CPR, k_col = tid % C::CPR;
+  const uint32_t k_goff = (uint32_t)k_row0 * C::ROW + k_col * 16;
+  const uint32_t k_soff = (uint32_t)k_row0 * C::KROW + k_col * 16;
+  constexpr int K_ROWS_PER_IT = C::NT / C::CPR;
+  // V staging: item tid -> 4-key group g, 16-byte column cc (waves past the
+  // last item skip the V work)
+  constexpr int V_WAVES = C::VITEMS < C::NT ? C::VITEMS / 64 : NWAVES;
+  const bool v_worker = wave < V_WAVES;
+  const int v_g = tid % (BN / 4), v_cc = tid / (BN / 4);
+  const uint32_t v_goff = (uint32_t)(4 * v_g) * C::ROW + v_cc * 16;
+  const uint32_t v_soff = C::KBYTES + (uint32_t)(v_cc * C::EPC) * C::VROW +
+                          (uint32_t)vt_pos<KPL>(4 * v_g) * ES;
+  // MFMA operand reads
+  const uint32_t k_roff = (uint32_t)l32 * C::KROW + hh * KPL * ES;
+  const uint32_t v_roff = C::KBYTES + (uint32_t)l32 * C::VROW + hh * KPL * ES;
+
   u32x4 kst[C::KPT];
   u32x4 vst[C::VPT][4];
 
   auto load_tile = [&](int j) {
-    const int kbase = j * BN;
+    const uint32_t kbase = (uint32_t)j * BN;
+    const uint32_t rem = head_bytes - kbase * C::ROW;     // bytes from this tile to the end
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (size_t)kbase * C::ROW, rem);
 #pragma unroll
-    for (int it = 0; it < C::KPT; ++it) {
-      const int ch = tid + it * C::NT;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      const int key = kbase + row;
-      kst[it] = (key < N) ? *(const u32x4*)(Kg + ((size_t)key * D * ES + cc * 16))
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int it = 0; it < C::KPT; ++it)
+      kst[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff + it * K_ROWS_PER_IT * C::ROW, 0, 0);
+    if (v_worker) {
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (size_t)kbase * C::ROW, rem);
 #pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-      const int item = tid + it * C::NT;
-      if (C::VITEMS % C::NT == 0 || item < C::VITEMS) {
-        const int g = item % (BN / 4), cc = item / (BN / 4);
+      for (int it = 0; it < C::VPT; ++it)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + 4 * g + i;
-          vst[it][i] = (key < N) ? *(const u32x4*)(Vg + ((size_t)key * D * ES + cc * 16))
-                                 : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+        for (int i = 0; i < 4; ++i)
+          vst[it][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              rv, v_goff + it * (C::NT / (BN / 4)) * 16 + i * C::ROW, 0, 0);
     }
   };
 
   auto store_tile = [&](int buf) {
-    unsigned char* Ks = smem + buf * C::STAGE;
-    unsigned char* Vs = Ks + C::KBYTES;
+    unsigned char* st = smem + buf * C::STAGE;
 #pragma unroll
-    for (int it = 0; it < C::KPT; ++it) {
-      const int ch = tid + it * C::NT;
-      const int row = ch / C::CPR, cc = ch % C::CPR;
-      *(u32x4*)(Ks + row * C::KROW + cc * 16) = kst[it];
-    }
+    for (int it = 0; it < C::KPT; ++it)
+      *(u32x4*)(st + k_soff + it * K_ROWS_PER_IT * C::KROW) = kst[it];
+    if (v_worker) {
 #pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-      const int item = tid + it * C::NT;
-      if (C::VITEMS % C::NT == 0 || item < C::VITEMS) {
-        const int g = item % (BN / 4), cc = item / (BN / 4);
-        // four consecutive keys land at four consecutive positions for bf16
-        // and fp8; fp32 positions are two apart
-        const int pos0 = vt_pos<KPL>(4 * g);
+      for (int it = 0; it < C::VPT; ++it) {
+        unsigned char* dst0 = st + v_soff + it * (C::NT / (BN / 4)) * C::EPC * C::VROW;
+        if constexpr (ES == 2) {
+          // element e of the chunk = half e%2 of dword e/2; four keys -> 8 bytes
 #pragma unroll
-        for (int e = 0; e < C::EPC; ++e) {
-          const int dcol = cc * C::EPC + e;
-          unsigned char* dst = Vs + dcol * C::VROW;
-          if constexpr (ES == 2) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            const uint32_t a0 = (vst[it][0][w] >> sh) & 0xffffu;
-            const uint32_t a1 = (vst[it][1][w] >> sh) & 0xffffu;
-            const uint32_t a2 = (vst[it][2][w] >> sh) & 0xffffu;
-            const uint32_t a3 = (vst[it][3][w] >> sh) & 0xffffu;
-            uint2 pk;
-            pk.x = a0 | (a1 << 16);
-            pk.y = a2 | (a3 << 16);
-            *(uint2*)(dst + pos0 * 2) = pk;
-          } else if constexpr (ES == 1) {
-            const int w = e >> 2, sh = (e & 3) * 8;
-            const uint32_t a0 = (vst[it][0][w] >> sh) & 0xffu;
-            const uint32_t a1 = (vst[it][1][w] >> sh) & 0xffu;
-            const uint32_t a2 = (vst[it][2][w] >> sh) & 0xffu;
-            const uint32_t a3 = (vst[it][3][w] >> sh) & 0xffu;
-            *(uint32_t*)(dst + pos0) = a0 | (a1 << 8) | (a2 << 16) | (a3 << 24);
-          } else {
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+              const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+              uint2 pk;
+              pk.x = perm(vst[it][1][w], vst[it][0][w], sel);
+              pk.y = perm(vst[it][3][w], vst[it][2][w], sel);
+              *(uint2*)(dst0 + (2 * w + hi) * C::VROW) = pk;
+            }
+        } else if constexpr (ES == 1) {
+          // 4x4 byte transpose of the four keys' dword w
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t t0 = perm(vst[it][1][w], vst[it][0][w], 0x05010400u);
+            const uint32_t t1 = perm(vst[it][3][w], vst[it][2][w], 0x05010400u);
+            const uint32_t t2 = perm(vst[it][1][w], vst[it][0][w], 0x07030602u);
+            const uint32_t t3 = perm(vst[it][3][w], vst[it][2][w], 0x07030602u);
+            *(uint32_t*)(dst0 + (4 * w + 0) * C::VROW) = perm(t1, t0, 0x05040100u);
+            *(uint32_t*)(dst0 + (4 * w + 1) * C::VROW) = perm(t1, t0, 0x07060302u);
+            *(uint32_t*)(dst0 + (4 * w + 2) * C::VROW) = perm(t3, t2, 0x05040100u);
+            *(uint32_t*)(dst0 + (4 * w + 3) * C::VROW) = perm(t3, t2, 0x07060302u);
+          }
+        } else {
+          // fp32: four keys land two positions apart
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              *(uint32_t*)(dst + vt_pos<KPL>(4 * g + i) * 4) = vst[it][i][e];
-          }
+              *(uint32_t*)(dst0 + e * C::VROW + (vt_pos<KPL>(4 * v_g + i) - vt_pos<KPL>(4 * v_g)) * 4) =
+                  vst[it][i][e];
         }
       }
     }
@@ -344,8 +392,7 @@ fa_fwd_kernel(FwdArgs p) {
     // a wave whose 32 rows all lie above this tile's first key skips it
     const bool wave_active = !CAUSAL || kbase <= q0w + 31;
     if (wave_active) {
-      const unsigned char* Ks = smem + buf * C::STAGE;
-      const unsigned char* Vs = Ks + C::KBYTES;
+      const unsigned char* st = smem + buf * C::STAGE;
 
       // S^T = K Q^T, one 32x32 block per 32 keys
       f32x16 s[C::NB];
@@ -353,27 +400,32 @@ fa_fwd_kernel(FwdArgs p) {
       for (int b = 0; b < C::NB; ++b) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
-        const unsigned char* krow = Ks + (32 * b + l32) * C::KROW + hh * KPL * ES;
 #pragma unroll
         for (int kk = 0; kk < C::QK_STEPS; ++kk) {
           Op a;
-          const uint32_t* src = (const uint32_t*)(krow + kk * 2 * KPL * ES);
+          const uint32_t* src = (const uint32_t*)(st + k_roff + b * 32 * C::KROW + kk * 2 * KPL * ES);
 #pragma unroll
           for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
           mfma<DT>(a, qop[kk], s[b]);
         }
       }
 
-      // masking, only on tiles that hold keys >= N or cross the diagonal
+      // masking, only on tiles that hold keys >= N or cross the diagonal.
+      // Key kbase + 4hh + rel (rel = 32b + 8jj + i, a compile-time constant per
+      // register) is valid iff rel < lim.
       const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0w);
+      int lim = N - kbase - 4 * hh;
+      if constexpr (CAUSAL) {
+        const int lim_c = my_q - kbase - 4 * hh + 1;
+        lim = lim < lim_c ? lim : lim_c;
+      }
       if (need_mask) {
 #pragma unroll
         for (int b = 0; b < C::NB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 32 * b + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= my_q);
-            s[b][r] = ok ? s[b][r] : masked_raw;
+            const int rel = 32 * b + 8 * (r >> 2) + (r & 3);
+            s[b][r] = rel < lim ? s[b][r] : masked_raw;
           }
       }
 
@@ -399,18 +451,18 @@ fa_fwd_kernel(FwdArgs p) {
       const float m_new = fmaxf(m_run, ext * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      const float m_sub = m_new - kPBias;
 
-      // p = exp2(s*c - m_new); masked keys give 0
+      // p = exp2(s*c - m_new) (times 256 for fp8); masked keys give 0
       float psum = 0.0f;
 #pragma unroll
       for (int b = 0; b < C::NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t = __builtin_fmaf(s[b][r], c, -m_new);
+          float t = __builtin_fmaf(s[b][r], c, -m_sub);
           if (need_mask) {
-            const int key = kbase + 32 * b + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= my_q);
-            t = ok ? t : -__builtin_inff();
+            const int rel = 32 * b + 8 * (r >> 2) + (r & 3);
+            t = rel < lim ? t : -__builtin_inff();
           }
           const float pv = __builtin_amdgcn_exp2f(t);
           s[b][r] = pv;
@@ -434,20 +486,17 @@ fa_fwd_kernel(FwdArgs p) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int r0 = n * KPL + 2 * w;
-            const float x0 = s[r0 >> 4][r0 & 15], x1 = s[(r0 + 1) >> 4][(r0 + 1) & 15];
-            const __bf16 b0 = (__bf16)x0, b1 = (__bf16)x1;
-            pop[n].w[w] = (uint32_t)__builtin_bit_cast(unsigned short, b0) |
-                          ((uint32_t)__builtin_bit_cast(unsigned short, b1) << 16);
+            pop[n].w[w] = pack_bf16(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15]);
           }
         } else if constexpr (DT == kFP8) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int r0 = n * KPL + 4 * w;
             int v = 0;
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15] * 256.0f,
-                                                s[(r0 + 1) >> 4][(r0 + 1) & 15] * 256.0f, v, false);
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15] * 256.0f,
-                                                s[(r0 + 3) >> 4][(r0 + 3) & 15] * 256.0f, v, true);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15],
+                                                s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
+            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15],
+                                                s[(r0 + 3) >> 4][(r0 + 3) & 15], v, true);
             pop[n].w[w] = (uint32_t)v;
           }
         } else {
@@ -459,11 +508,11 @@ fa_fwd_kernel(FwdArgs p) {
       // O^T += V^T P^T
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const unsigned char* vrow = Vs + (32 * mb + l32) * C::VROW + hh * KPL * ES;
 #pragma unroll
         for (int n = 0; n < C::PV_STEPS; ++n) {
           Op a;
-          const uint32_t* src = (const uint32_t*)(vrow + n * 2 * KPL * ES);
+          const uint32_t* src =
+              (const uint32_t*)(st + v_roff + mb * 32 * C::VROW + n * 2 * KPL * ES);
 #pragma unroll
           for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
           mfma<DT>(a, pop[n], oacc[mb]);
@@ -477,10 +526,11 @@ fa_fwd_kernel(FwdArgs p) {
 
   // ---- epilogue: full row sum, L, O / l, bounded stores ----
   const float l_tot = swap_halves_sum(l_run);
-  const float inv = pv_scale / l_tot;
+  const float inv = dv / l_tot;
   if (my_q < N) {
     if (hh == 0)
-      p.lse[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+      p.lse[(size_t)bh * N + my_q] =
+          (m_run - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
     const size_t obase = ((size_t)bh * N + my_q) * D;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
@@ -492,12 +542,9 @@ fa_fwd_kernel(FwdArgs p) {
         if constexpr (DT == kF32) {
           *(float4*)((float*)p.o + obase + d0) = make_float4(x0, x1, x2, x3);
         } else {
-          const __bf16 b0 = (__bf16)x0, b1 = (__bf16)x1, b2 = (__bf16)x2, b3 = (__bf16)x3;
           uint2 pk;
-          pk.x = (uint32_t)__builtin_bit_cast(unsigned short, b0) |
-                 ((uint32_t)__builtin_bit_cast(unsigned short, b1) << 16);
-          pk.y = (uint32_t)__builtin_bit_cast(unsigned short, b2) |
-                 ((uint32_t)__builtin_bit_cast(unsigned short, b3) << 16);
+          pk.x = pack_bf16(x0, x1);
+          pk.y = pack_bf16(x2, x3);
           *(uint2*)((unsigned short*)p.o + obase + d0) = pk;
         }
       }
