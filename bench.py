@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a kernel of known "
+                         "traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
@@ -130,6 +133,16 @@ def main():
 
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, "f32" if w.dtype == "f32" else "bf16", seed=0)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)

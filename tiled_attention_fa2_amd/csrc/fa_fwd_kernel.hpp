@@ -189,6 +189,39 @@ __host__ __device__ __forceinline__ void work_item(int bid, int total, int n_qti
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
+// Pairwise reduction of n values (n a power of two): depth log2(n) instead of
+// a chain of n - 1 dependent operations.
+template <int NV, typename Get, typename Op2>
+__device__ __forceinline__ float tree_reduce(Get get, Op2 op) {
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = get(i);
+#pragma unroll
+  for (int w = NV / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) v[i] = op(v[i], v[i + w]);
+  return v[0];
+}
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
+// Max of n values (n a multiple of 8) as four interleaved chains of
+// three-input maxima (v_max3_f32): about n/2 instructions, short chains.
+template <int NV, typename Get>
+__device__ __forceinline__ float max_reduce(Get get) {
+  static_assert(NV % 8 == 0, "max_reduce takes a multiple of 8 values");
+  float m0 = fmaxf(get(0), get(1)), m1 = fmaxf(get(2), get(3));
+  float m2 = fmaxf(get(4), get(5)), m3 = fmaxf(get(6), get(7));
+#pragma unroll
+  for (int i = 8; i < NV; i += 8) {
+    m0 = fmaxf(fmaxf(m0, get(i + 0)), get(i + 1));
+    m1 = fmaxf(fmaxf(m1, get(i + 2)), get(i + 3));
+    m2 = fmaxf(fmaxf(m2, get(i + 4)), get(i + 5));
+    m3 = fmaxf(fmaxf(m3, get(i + 6)), get(i + 7));
+  }
+  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+}
+
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return
 // zero, which is how rows past the end of a head read as zeros without a
 // branch. 0x00020000 is the gfx9 raw-buffer word 3 (32-bit data format).
@@ -252,8 +285,19 @@ fa_fwd_kernel(FwdArgs p) {
   // RTX 5080", section "P goes through shared memory"): exp2(t + 8) = 256 exp2(t),
   // folded into the subtraction of the running max at no cost.
   constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
-  const bool c_nonneg = c >= 0.0f;
-  const float masked_raw = c_nonneg ? -__builtin_inff() : __builtin_inff();
+  // Conditional rescale ("Kernels and Memory in LLM Inference", section
+  // "FlashAttention-4"): the reference max may move only when a tile's max
+  // beats it by more than kTau (log2 units), saving O rescales. It is kept at
+  // 0 (exact running max): with a stale reference the dominant weight of a
+  // near one-hot row is 2^delta instead of exactly 1, and its bf16 rounding
+  // adds up to 2^-9 |v| to the output error (measured on peaked inputs).
+  constexpr float kTau = 0.0f;
+  // scale == 0: every valid score gets the same weight. A tiny positive c
+  // gives exactly that (|s * c| < 2^-24, so exp2 rounds to 1) and lets a
+  // masked score be -inf rather than -inf * 0 = NaN.
+  if (c == 0.0f) c = 1e-30f;
+  const bool c_pos = c > 0.0f;
+  const float masked_raw = c_pos ? -__builtin_inff() : __builtin_inff();
 
   // ---- Q^T operands, held in registers for the whole loop ----
   Op qop[C::QK_STEPS];
@@ -394,32 +438,38 @@ fa_fwd_kernel(FwdArgs p) {
     if (wave_active) {
       const unsigned char* st = smem + buf * C::STAGE;
 
-      // S^T = K Q^T, one 32x32 block per 32 keys
+      // S^T = K Q^T, one 32x32 block per 32 keys; the blocks alternate so that
+      // consecutive MFMAs never wait on each other's accumulator
       f32x16 s[C::NB];
 #pragma unroll
-      for (int b = 0; b < C::NB; ++b) {
+      for (int b = 0; b < C::NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < C::QK_STEPS; ++kk) {
+      for (int kk = 0; kk < C::QK_STEPS; ++kk)
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
           Op a;
           const uint32_t* src = (const uint32_t*)(st + k_roff + b * 32 * C::KROW + kk * 2 * KPL * ES);
 #pragma unroll
           for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
           mfma<DT>(a, qop[kk], s[b]);
         }
-      }
 
-      // masking, only on tiles that hold keys >= N or cross the diagonal.
-      // Key kbase + 4hh + rel (rel = 32b + 8jj + i, a compile-time constant per
-      // register) is valid iff rel < lim.
+      // Masking, only on tiles that hold keys >= N or cross the diagonal: a
+      // masked score becomes -inf after scaling (c != 0 here), so it drops out
+      // of the max and exp2 turns it into p = 0. Key kbase + 4hh + rel (rel =
+      // 32b + 8jj + i, a compile-time constant per register) is valid iff
+      // rel < lim. The empty asm keeps this a real branch: otherwise the
+      // compiler turns it into selects that run on every tile.
       const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0w);
-      int lim = N - kbase - 4 * hh;
-      if constexpr (CAUSAL) {
-        const int lim_c = my_q - kbase - 4 * hh + 1;
-        lim = lim < lim_c ? lim : lim_c;
-      }
       if (need_mask) {
+        asm volatile("" ::: "memory");
+        int lim = N - kbase - 4 * hh;
+        if constexpr (CAUSAL) {
+          const int lim_c = my_q - kbase - 4 * hh + 1;
+          lim = lim < lim_c ? lim : lim_c;
+        }
 #pragma unroll
         for (int b = 0; b < C::NB; ++b)
 #pragma unroll
@@ -429,48 +479,37 @@ fa_fwd_kernel(FwdArgs p) {
           }
       }
 
-      // row extreme of the raw scores (max when c >= 0, min when c < 0)
+      // row extreme of the raw scores (max when c > 0, min when c < 0)
       float ext;
-      if (c_nonneg) {
-        ext = s[0][0];
-#pragma unroll
-        for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[b][r]);
+      if (c_pos) {
+        ext = max_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; });
         ext = swap_halves_max(ext);
       } else {
-        ext = s[0][0];
-#pragma unroll
-        for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ext = fminf(ext, s[b][r]);
+        ext = -max_reduce<C::NB * 16>([&](int i) { return -s[i >> 4][i & 15]; });
         ext = swap_halves_min(ext);
       }
-      // every processed (row, tile) pair holds at least one valid key, so ext
-      // is finite and so is m_new
-      const float m_new = fmaxf(m_run, ext * c);
+      // every processed (row, tile) pair holds at least one valid key, so
+      // m_tile is finite. The reference max moves only when this tile's max
+      // exceeds it by more than kTau (log2 units); until then p <= 2^kTau and
+      // O needs no rescale. l and O always share the reference, so the result
+      // is unchanged.
+      const float m_tile = ext * c;
+      const float m_new = m_tile > m_run + kTau ? fmaxf(m_run, m_tile) : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       const float m_sub = m_new - kPBias;
 
-      // p = exp2(s*c - m_new) (times 256 for fp8); masked keys give 0
-      float psum = 0.0f;
+      // p = exp2(s*c - m_ref) (times 256 for fp8)
 #pragma unroll
       for (int b = 0; b < C::NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = __builtin_fmaf(s[b][r], c, -m_sub);
-          if (need_mask) {
-            const int rel = 32 * b + 8 * (r >> 2) + (r & 3);
-            t = rel < lim ? t : -__builtin_inff();
-          }
-          const float pv = __builtin_amdgcn_exp2f(t);
-          s[b][r] = pv;
-          psum += pv;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
+      const float psum = tree_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; },
+                                                 [](float x, float y) { return x + y; });
       l_run = alpha * l_run + psum;
 
-      // O^T *= alpha (skipped when the max did not move for any row of the wave)
+      // O^T *= alpha (skipped when the reference did not move for any row of the wave)
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb)
@@ -505,11 +544,11 @@ fa_fwd_kernel(FwdArgs p) {
         }
       }
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T, the d-blocks alternating between consecutive MFMAs
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
+      for (int n = 0; n < C::PV_STEPS; ++n) {
 #pragma unroll
-        for (int n = 0; n < C::PV_STEPS; ++n) {
+        for (int mb = 0; mb < C::MB; ++mb) {
           Op a;
           const uint32_t* src =
               (const uint32_t*)(st + v_roff + mb * 32 * C::VROW + n * 2 * KPL * ES);
