@@ -37,6 +37,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def kernel_name(w) -> str:
+    """The kernel fa_fwd launches for this workload (head dim 128 bf16 / fp8
+    use the DMA + transpose-read kernel)."""
+    return "fa_fwd_dma_kernel" if (w.d == 128 and w.dtype in ("bf16", "fp8")) else "fa_fwd_kernel"
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, only if
     it was taken on the current kernel source."""
@@ -169,7 +175,7 @@ def main():
                    "wall_ms_per_step": round(wall_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "fa_fwd_kernel", "kernel_ms": round(kern_ms, 4)},
+                     "kernel": kernel_name(w), "kernel_ms": round(kern_ms, 4)},
     }
 
     if not a.no_fp8 and w.dtype == "bf16" and w.name.startswith("bf16_dit"):
@@ -196,7 +202,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(w8.flops() / (kern8 * 1e-3) / 1e12, 2),
                          "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                          "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
-                         "traffic": measured_traffic(w8.name), "kernel": "fa_fwd_kernel",
+                         "traffic": measured_traffic(w8.name), "kernel": kernel_name(w8),
                          "kernel_ms": round(kern8, 4)},
         }
 
