@@ -613,712 +613,6 @@ fa_fwd_kernel(FwdArgs p) {
 
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant: one workgroup of 8 waves = 256 query rows, two groups of
-// four waves (one wave of each group per SIMD). Phases separated by workgroup
-// barriers alternate the groups between
-//   G(j): the MFMA phase, O^T += V_{j-1}^T P_{j-1}^T and S_j^T = K_j Q^T, and
-//   S(j): the softmax phase on S_j (max, exp2, row sum, O rescale, pack P_j),
-// so that on every SIMD one wave feeds the matrix core while the other runs
-// the softmax. Per tile j:
-//   phase 2j   : group 0 runs G(j), group 1 runs S(j-1); stage j+1 is fetched
-//   phase 2j+1 : group 0 runs S(j), group 1 runs G(j);   stage j+1 is stored
-// LDS stage j (buffer j&1) holds K_j and V_{j-1}, the operands of G(j). This
-// is the FA-2 split of the queries over warps ("Kernels and Memory in LLM
-// Inference", section "FlashAttention-2") with the FA-3 idea of overlapping
-// the softmax of one warp group with the matrix work of another (section
-// "FlashAttention-3"), built with plain workgroup barriers.
-template <int DT, int D, int BN, bool CAUSAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_pp_kernel(FwdArgs p) {
-  constexpr int NWAVES = 8;
-  using C = Cfg<DT, D, BN, NWAVES>;
-  using Op = Operand<DT>;
-  constexpr int ES = C::ES, KPL = C::KPL;
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-  const int group = wave >> 2;
-
-  int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_qtiles, p.n_qtiles, CAUSAL ? 1 : 0, bh, qt);
-  const int N = p.N;
-  const int q0 = qt * C::BM;
-  const int q0w = q0 + 128 * group + 32 * (wave & 3);
-  const int my_q = q0w + l32;
-
-  const uint32_t head_bytes = (uint32_t)N * C::ROW;   // < 2^31, checked by the host
-  const size_t head_off = (size_t)bh * head_bytes;
-  const unsigned char* Qg = (const unsigned char*)p.q + head_off;
-  const unsigned char* Kg = (const unsigned char*)p.k + head_off;
-  const unsigned char* Vg = (const unsigned char*)p.v + head_off;
-
-  float c = p.scale * 1.4426950408889634f;
-  float dv = 1.0f;
-  if constexpr (DT == kFP8) {
-    c *= p.descales[bh] * p.descales[p.BH + bh];
-    dv = p.descales[2 * p.BH + bh];
-  }
-  constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
-  if (c == 0.0f) c = 1e-30f;
-  const bool c_pos = c > 0.0f;
-  const float masked_raw = c_pos ? -__builtin_inff() : __builtin_inff();
-
-  // ---- Q^T operands ----
-  Op qop[C::QK_STEPS];
-  {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg, head_bytes);
-    const uint32_t qoff = (uint32_t)my_q * C::ROW + hh * KPL * ES;
-#pragma unroll
-    for (int kk = 0; kk < C::QK_STEPS; ++kk) {
-      const uint32_t off = qoff + kk * 2 * KPL * ES;
-      if constexpr (Op::DW >= 4) {
-#pragma unroll
-        for (int x = 0; x < Op::DW / 4; ++x) {
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16 * x, 0, 0);
-#pragma unroll
-          for (int y = 0; y < 4; ++y) qop[kk].w[4 * x + y] = w[y];
-        }
-      } else {
-        qop[kk].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
-      }
-    }
-  }
-
-  // ---- key-tile range: T tiles for the workgroup, tiles 0..last_w for this wave ----
-  int T = (N + BN - 1) / BN;
-  if constexpr (CAUSAL) {
-    const int last = (q0 + C::BM - 1) / BN + 1;
-    T = T < last ? T : last;
-  }
-  int last_w = T - 1;
-  if constexpr (CAUSAL) {
-    const int lw = (q0w + 31) / BN;
-    last_w = lw < last_w ? lw : last_w;
-  }
-
-  // ---- staging: K chunks over all threads, V items over the first V_WAVES waves ----
-  const int k_row0 = tid / C::CPR, k_col = tid % C::CPR;
-  const uint32_t k_goff = (uint32_t)k_row0 * C::ROW + k_col * 16;
-  const uint32_t k_soff = (uint32_t)k_row0 * C::KROW + k_col * 16;
-  constexpr int K_ROWS_PER_IT = C::NT / C::CPR > 0 ? C::NT / C::CPR : 1;
-  constexpr bool K_ALL = C::KCHUNKS % C::NT == 0;
-  const bool k_worker = K_ALL || tid < C::KCHUNKS;
-  constexpr int V_WAVES = C::VITEMS < C::NT ? C::VITEMS / 64 : NWAVES;
-  const bool v_worker = wave < V_WAVES;
-  const int v_g = tid % (BN / 4), v_cc = tid / (BN / 4);
-  const uint32_t v_goff = (uint32_t)(4 * v_g) * C::ROW + v_cc * 16;
-  const uint32_t v_soff = C::KBYTES + (uint32_t)(v_cc * C::EPC) * C::VROW +
-                          (uint32_t)vt_pos<KPL>(4 * v_g) * ES;
-  const uint32_t k_roff = (uint32_t)l32 * C::KROW + hh * KPL * ES;
-  const uint32_t v_roff = C::KBYTES + (uint32_t)l32 * C::VROW + hh * KPL * ES;
-  static_assert(C::VPT == 1, "one V item per thread at most");
-
-  u32x4 kst[C::KPT];
-  u32x4 vst[4];
-
-  auto load_k = [&](int jt) {
-    const uint32_t kbase = (uint32_t)jt * BN;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (size_t)kbase * C::ROW, head_bytes - kbase * C::ROW);
-    if (k_worker) {
-#pragma unroll
-      for (int it = 0; it < C::KPT; ++it)
-        kst[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff + it * K_ROWS_PER_IT * C::ROW, 0, 0);
-    }
-  };
-  auto load_v = [&](int jt) {
-    const uint32_t kbase = (uint32_t)jt * BN;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (size_t)kbase * C::ROW, head_bytes - kbase * C::ROW);
-    if (v_worker) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + i * C::ROW, 0, 0);
-    }
-  };
-  auto store_k = [&](int b) {
-    unsigned char* st = smem + b * C::STAGE;
-    if (k_worker) {
-#pragma unroll
-      for (int it = 0; it < C::KPT; ++it)
-        *(u32x4*)(st + k_soff + it * K_ROWS_PER_IT * C::KROW) = kst[it];
-    }
-  };
-  auto store_v = [&](int b) {
-    unsigned char* dst0 = smem + b * C::STAGE + v_soff;
-    if (v_worker) {
-      if constexpr (ES == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-            uint2 pk;
-            pk.x = perm(vst[1][w], vst[0][w], sel);
-            pk.y = perm(vst[3][w], vst[2][w], sel);
-            *(uint2*)(dst0 + (2 * w + hi) * C::VROW) = pk;
-          }
-      } else if constexpr (ES == 1) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t t0 = perm(vst[1][w], vst[0][w], 0x05010400u);
-          const uint32_t t1 = perm(vst[3][w], vst[2][w], 0x05010400u);
-          const uint32_t t2 = perm(vst[1][w], vst[0][w], 0x07030602u);
-          const uint32_t t3 = perm(vst[3][w], vst[2][w], 0x07030602u);
-          *(uint32_t*)(dst0 + (4 * w + 0) * C::VROW) = perm(t1, t0, 0x05040100u);
-          *(uint32_t*)(dst0 + (4 * w + 1) * C::VROW) = perm(t1, t0, 0x07060302u);
-          *(uint32_t*)(dst0 + (4 * w + 2) * C::VROW) = perm(t3, t2, 0x05040100u);
-          *(uint32_t*)(dst0 + (4 * w + 3) * C::VROW) = perm(t3, t2, 0x07060302u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(uint32_t*)(dst0 + e * C::VROW + (vt_pos<KPL>(4 * v_g + i) - vt_pos<KPL>(4 * v_g)) * 4) =
-                vst[i][e];
-      }
-    }
-  };
-
-  // ---- per-wave state ----
-  f32x16 oacc[C::MB];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.0f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-  f32x16 s[C::NB];      // S_j, from G(j) to S(j)
-  Op pop[C::PV_STEPS];  // P_j, from S(j) to G(j+1)
-
-  // ds_reads per MFMA operand: 16-byte reads, or one 4-byte read for fp32
-  constexpr int kReadsPerOp = Op::DW >= 4 ? Op::DW / 4 : 1;
-  // G(j): PV of tile j-1, then QK of tile j, operands from stage j (buffer j&1)
-  auto gemm_phase = [&](int jt) {
-    const unsigned char* st = smem + (jt & 1) * C::STAGE;
-    if (jt >= 1 && jt - 1 <= last_w) {
-#pragma unroll
-      for (int n = 0; n < C::PV_STEPS; ++n)
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          Op a;
-          const uint32_t* src =
-              (const uint32_t*)(st + v_roff + mb * 32 * C::VROW + n * 2 * KPL * ES);
-#pragma unroll
-          for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
-          mfma<DT>(a, pop[n], oacc[mb]);
-        }
-      interleave_reads_with_mfma<C::PV_STEPS * C::MB, kReadsPerOp, 2>();
-    }
-    if (jt < T && jt <= last_w) {
-#pragma unroll
-      for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[b][r] = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < C::QK_STEPS; ++kk)
-#pragma unroll
-        for (int b = 0; b < C::NB; ++b) {
-          Op a;
-          const uint32_t* src = (const uint32_t*)(st + k_roff + b * 32 * C::KROW + kk * 2 * KPL * ES);
-#pragma unroll
-          for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
-          mfma<DT>(a, qop[kk], s[b]);
-        }
-      interleave_reads_with_mfma<C::QK_STEPS * C::NB, kReadsPerOp, 2>();
-    }
-  };
-
-  // S(j): online softmax of S_j, rescale of O, P_j packed for the next G
-  auto softmax_phase = [&](int jt) {
-    if (jt > last_w) return;
-    const int kbase = jt * BN;
-    const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0w);
-    if (need_mask) {
-      asm volatile("" ::: "memory");
-      int lim = N - kbase - 4 * hh;
-      if constexpr (CAUSAL) {
-        const int lim_c = my_q - kbase - 4 * hh + 1;
-        lim = lim < lim_c ? lim : lim_c;
-      }
-#pragma unroll
-      for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = 32 * b + 8 * (r >> 2) + (r & 3);
-          s[b][r] = rel < lim ? s[b][r] : masked_raw;
-        }
-    }
-    float ext;
-    if (c_pos) {
-      ext = max_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; });
-      ext = swap_halves_max(ext);
-    } else {
-      ext = -max_reduce<C::NB * 16>([&](int i) { return -s[i >> 4][i & 15]; });
-      ext = swap_halves_min(ext);
-    }
-    const float m_new = fmaxf(m_run, ext * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float m_sub = m_new - kPBias;
-#pragma unroll
-    for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
-    const float psum = tree_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; },
-                                               [](float x, float y) { return x + y; });
-    l_run = alpha * l_run + psum;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-    }
-#pragma unroll
-    for (int n = 0; n < C::PV_STEPS; ++n) {
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = n * KPL + 2 * w;
-          pop[n].w[w] = pack_bf16(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15]);
-        }
-      } else if constexpr (DT == kFP8) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int r0 = n * KPL + 4 * w;
-          int v = 0;
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15],
-                                              s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15],
-                                              s[(r0 + 3) >> 4][(r0 + 3) & 15], v, true);
-          pop[n].w[w] = (uint32_t)v;
-        }
-      } else {
-        pop[n].w[0] = f2u(s[n >> 4][n & 15]);
-      }
-    }
-  };
-
-  // prologue: stage 0 = K_0
-  load_k(0);
-  store_k(0);
-  __syncthreads();
-
-  for (int j = 0; j <= T; ++j) {
-    const int nb = (j + 1) & 1;
-    // ---- phase 2j: fetch stage j+1 = {K_{j+1}, V_j} ----
-    if (j + 1 < T) load_k(j + 1);
-    if (j < T) load_v(j);
-    if (group == 0)
-      gemm_phase(j);
-    else if (j >= 1)
-      softmax_phase(j - 1);
-    __syncthreads();
-    // ---- phase 2j+1: store stage j+1 into the buffer stage j-1 used ----
-    if (j + 1 < T) store_k(nb);
-    if (j < T) store_v(nb);
-    if (group == 0) {
-      if (j < T) softmax_phase(j);
-    } else {
-      gemm_phase(j);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue ----
-  const float l_tot = swap_halves_sum(l_run);
-  const float inv = dv / l_tot;
-  if (my_q < N) {
-    if (hh == 0)
-      p.lse[(size_t)bh * N + my_q] =
-          (m_run - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
-    const size_t obase = ((size_t)bh * N + my_q) * D;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = 32 * mb + 8 * jj + 4 * hh;
-        const float x0 = oacc[mb][4 * jj + 0] * inv, x1 = oacc[mb][4 * jj + 1] * inv;
-        const float x2 = oacc[mb][4 * jj + 2] * inv, x3 = oacc[mb][4 * jj + 3] * inv;
-        if constexpr (DT == kF32) {
-          *(float4*)((float*)p.o + obase + d0) = make_float4(x0, x1, x2, x3);
-        } else {
-          uint2 pk;
-          pk.x = pack_bf16(x0, x1);
-          pk.y = pack_bf16(x2, x3);
-          *(uint2*)((unsigned short*)p.o + obase + d0) = pk;
-        }
-      }
-  }
-}
-
-
-// ---------------------------------------------------------------------------
-// Software-pipelined variant: each wave issues the QK MFMAs of key tile j+1
-// while it runs the softmax of tile j, so its matrix work and its vector work
-// interleave instead of alternating in bursts. LDS stage b = (j+1)&1 holds
-// K_{j+1} and V_j during iteration j; stage j&1 is refilled with K_{j+2} and
-// V_{j+1}. Two score buffers alternate between "being produced by MFMA" and
-// "being turned into P"; the loop is unrolled by two so they swap roles
-// without register copies.
-template <int DT, int D, int BN, int NWAVES, bool CAUSAL, int LOOK>
-__global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_sp_kernel(FwdArgs p) {
-  using C = Cfg<DT, D, BN, NWAVES>;
-  using Op = Operand<DT>;
-  constexpr int ES = C::ES, KPL = C::KPL;
-  constexpr int kReadsPerOp = Op::DW >= 4 ? Op::DW / 4 : 1;
-
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_qtiles, p.n_qtiles, CAUSAL ? 1 : 0, bh, qt);
-  const int N = p.N;
-  const int q0 = qt * C::BM;
-  const int q0w = q0 + 32 * wave;
-  const int my_q = q0w + l32;
-
-  const uint32_t head_bytes = (uint32_t)N * C::ROW;
-  const size_t head_off = (size_t)bh * head_bytes;
-  const unsigned char* Qg = (const unsigned char*)p.q + head_off;
-  const unsigned char* Kg = (const unsigned char*)p.k + head_off;
-  const unsigned char* Vg = (const unsigned char*)p.v + head_off;
-
-  float c = p.scale * 1.4426950408889634f;
-  float dv = 1.0f;
-  if constexpr (DT == kFP8) {
-    c *= p.descales[bh] * p.descales[p.BH + bh];
-    dv = p.descales[2 * p.BH + bh];
-  }
-  constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
-  // A negative scale is folded into Q: S = (-Q) K^T times |c|. Flipping the
-  // sign bits of the Q operands is exact in every format, and leaves one
-  // softmax path (row max, masked scores at -inf).
-  const bool neg_scale = c < 0.0f;
-  c = fabsf(c);
-  if (c == 0.0f) c = 1e-30f;
-  constexpr float masked_raw = -__builtin_inff();
-
-  Op qop[C::QK_STEPS];
-  {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg, head_bytes);
-    const uint32_t qoff = (uint32_t)my_q * C::ROW + hh * KPL * ES;
-#pragma unroll
-    for (int kk = 0; kk < C::QK_STEPS; ++kk) {
-      const uint32_t off = qoff + kk * 2 * KPL * ES;
-      if constexpr (Op::DW >= 4) {
-#pragma unroll
-        for (int x = 0; x < Op::DW / 4; ++x) {
-          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16 * x, 0, 0);
-#pragma unroll
-          for (int y = 0; y < 4; ++y) qop[kk].w[4 * x + y] = w[y];
-        }
-      } else {
-        qop[kk].w[0] = __builtin_amdgcn_raw_buffer_load_b32(rq, off, 0, 0);
-      }
-    }
-    if (neg_scale) {
-      constexpr uint32_t sign = ES == 4 ? 0x80000000u : ES == 2 ? 0x80008000u : 0x80808080u;
-#pragma unroll
-      for (int kk = 0; kk < C::QK_STEPS; ++kk)
-#pragma unroll
-        for (int w = 0; w < Op::DW; ++w) qop[kk].w[w] ^= sign;
-    }
-  }
-
-  int T = (N + BN - 1) / BN;
-  if constexpr (CAUSAL) {
-    const int last = (q0 + C::BM - 1) / BN + 1;
-    T = T < last ? T : last;
-  }
-
-  const int k_row0 = tid / C::CPR, k_col = tid % C::CPR;
-  const uint32_t k_goff = (uint32_t)k_row0 * C::ROW + k_col * 16;
-  const uint32_t k_soff = (uint32_t)k_row0 * C::KROW + k_col * 16;
-  constexpr int K_ROWS_PER_IT = C::NT / C::CPR > 0 ? C::NT / C::CPR : 1;
-  constexpr bool K_ALL = C::KCHUNKS % C::NT == 0;
-  const bool k_worker = K_ALL || tid < C::KCHUNKS;
-  constexpr int V_WAVES = C::VITEMS < C::NT ? C::VITEMS / 64 : NWAVES;
-  const bool v_worker = wave < V_WAVES;
-  const int v_g = tid % (BN / 4), v_cc = tid / (BN / 4);
-  const uint32_t v_goff = (uint32_t)(4 * v_g) * C::ROW + v_cc * 16;
-  const uint32_t v_soff = C::KBYTES + (uint32_t)(v_cc * C::EPC) * C::VROW +
-                          (uint32_t)vt_pos<KPL>(4 * v_g) * ES;
-  const uint32_t k_roff = (uint32_t)l32 * C::KROW + hh * KPL * ES;
-  const uint32_t v_roff = C::KBYTES + (uint32_t)l32 * C::VROW + hh * KPL * ES;
-  static_assert(C::VPT == 1, "one V item per thread at most");
-
-  u32x4 kst[C::KPT];
-  u32x4 vst[4];
-
-  auto load_k = [&](int jt) {
-    const uint32_t kbase = (uint32_t)jt * BN;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (size_t)kbase * C::ROW, head_bytes - kbase * C::ROW);
-    if (k_worker) {
-#pragma unroll
-      for (int it = 0; it < C::KPT; ++it)
-        kst[it] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_goff + it * K_ROWS_PER_IT * C::ROW, 0, 0);
-    }
-  };
-  auto load_v = [&](int jt) {
-    const uint32_t kbase = (uint32_t)jt * BN;
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (size_t)kbase * C::ROW, head_bytes - kbase * C::ROW);
-    if (v_worker) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vst[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_goff + i * C::ROW, 0, 0);
-    }
-  };
-  auto store_k = [&](int b) {
-    unsigned char* st = smem + b * C::STAGE;
-    if (k_worker) {
-#pragma unroll
-      for (int it = 0; it < C::KPT; ++it)
-        *(u32x4*)(st + k_soff + it * K_ROWS_PER_IT * C::KROW) = kst[it];
-    }
-  };
-  auto store_v = [&](int b) {
-    unsigned char* dst0 = smem + b * C::STAGE + v_soff;
-    if (v_worker) {
-      if constexpr (ES == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-#pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-            uint2 pk;
-            pk.x = perm(vst[1][w], vst[0][w], sel);
-            pk.y = perm(vst[3][w], vst[2][w], sel);
-            *(uint2*)(dst0 + (2 * w + hi) * C::VROW) = pk;
-          }
-      } else if constexpr (ES == 1) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t t0 = perm(vst[1][w], vst[0][w], 0x05010400u);
-          const uint32_t t1 = perm(vst[3][w], vst[2][w], 0x05010400u);
-          const uint32_t t2 = perm(vst[1][w], vst[0][w], 0x07030602u);
-          const uint32_t t3 = perm(vst[3][w], vst[2][w], 0x07030602u);
-          *(uint32_t*)(dst0 + (4 * w + 0) * C::VROW) = perm(t1, t0, 0x05040100u);
-          *(uint32_t*)(dst0 + (4 * w + 1) * C::VROW) = perm(t1, t0, 0x07060302u);
-          *(uint32_t*)(dst0 + (4 * w + 2) * C::VROW) = perm(t3, t2, 0x05040100u);
-          *(uint32_t*)(dst0 + (4 * w + 3) * C::VROW) = perm(t3, t2, 0x07060302u);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(uint32_t*)(dst0 + e * C::VROW + (vt_pos<KPL>(4 * v_g + i) - vt_pos<KPL>(4 * v_g)) * 4) =
-                vst[i][e];
-      }
-    }
-  };
-
-  f32x16 oacc[C::MB];
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.0f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-  f32x16 sa[C::NB], sb[C::NB];
-
-  // S_jt = K_jt Q^T from stage b
-  auto qk = [&](f32x16 (&s)[C::NB], int b) {
-    const unsigned char* st = smem + b * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::NB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[i][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < C::QK_STEPS; ++kk)
-#pragma unroll
-      for (int i = 0; i < C::NB; ++i) {
-        Op a;
-        const uint32_t* src = (const uint32_t*)(st + k_roff + i * 32 * C::KROW + kk * 2 * KPL * ES);
-#pragma unroll
-        for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
-        mfma<DT>(a, qop[kk], s[i]);
-      }
-  };
-
-  // softmax of S_jt in place -> P_jt operands; updates m, l and rescales O
-  auto softmax = [&](f32x16 (&s)[C::NB], Op (&pop)[C::PV_STEPS], int jt) {
-    const int kbase = jt * BN;
-    const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0w);
-    if (need_mask) {
-      asm volatile("" ::: "memory");
-      int lim = N - kbase - 4 * hh;
-      if constexpr (CAUSAL) {
-        const int lim_c = my_q - kbase - 4 * hh + 1;
-        lim = lim < lim_c ? lim : lim_c;
-      }
-#pragma unroll
-      for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rel = 32 * b + 8 * (r >> 2) + (r & 3);
-          s[b][r] = rel < lim ? s[b][r] : masked_raw;
-        }
-    }
-    const float ext = swap_halves_max(max_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; }));
-    const float m_new = fmaxf(m_run, ext * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float m_sub = m_new - kPBias;
-    // exp2 in place, summed on the fly into four partial sums
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int b = 0; b < C::NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
-        ps[r & 3] += s[b][r];
-      }
-    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    l_run = alpha * l_run + psum;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-    }
-#pragma unroll
-    for (int n = 0; n < C::PV_STEPS; ++n) {
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = n * KPL + 2 * w;
-          pop[n].w[w] = pack_bf16(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15]);
-        }
-      } else if constexpr (DT == kFP8) {
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int r0 = n * KPL + 4 * w;
-          int v = 0;
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15],
-                                              s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
-          v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15],
-                                              s[(r0 + 3) >> 4][(r0 + 3) & 15], v, true);
-          pop[n].w[w] = (uint32_t)v;
-        }
-      } else {
-        pop[n].w[0] = f2u(s[n >> 4][n & 15]);
-      }
-    }
-  };
-
-  // O += P_jt V_jt from stage b
-  auto pv = [&](Op (&pop)[C::PV_STEPS], int b) {
-    const unsigned char* st = smem + b * C::STAGE;
-#pragma unroll
-    for (int n = 0; n < C::PV_STEPS; ++n)
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        Op a;
-        const uint32_t* src = (const uint32_t*)(st + v_roff + mb * 32 * C::VROW + n * 2 * KPL * ES);
-#pragma unroll
-        for (int w = 0; w < Op::DW; ++w) a.w[w] = src[w];
-        mfma<DT>(a, pop[n], oacc[mb]);
-      }
-  };
-
-  // One pipelined step: S_next = QK(j+1) issued alongside softmax(j) of
-  // S_cur, then PV(j); stage b = (j+1)&1 holds K_{j+1} and V_j. The last
-  // tile's step has no QK. Every S buffer is written unconditionally before it
-  // is read, which keeps only one of them live across a step boundary.
-  // Causal tiles above a wave's rows are computed and fully masked: their row
-  // max is -inf, so alpha = 1 and every p = 0.
-  auto step = [&](f32x16 (&s_cur)[C::NB], f32x16 (&s_next)[C::NB], int jt, auto has_next_tag) {
-    constexpr bool kNext = decltype(has_next_tag)::value;
-    const int b = (jt + 1) & 1;
-    const bool more = jt + 2 < T;
-    if (more) load_k(jt + 2);
-    if (kNext) load_v(jt + 1);
-    Op pop[C::PV_STEPS];
-    if constexpr (kNext) qk(s_next, b);
-    softmax(s_cur, pop, jt);
-    if constexpr (kNext) {
-      // interleave the QK MFMAs with their operand reads; the softmax's
-      // vector instructions fill the gaps
-      __builtin_amdgcn_sched_group_barrier(0x100, LOOK * kReadsPerOp, 0);
-#pragma unroll
-      for (int i = 0; i < C::QK_STEPS * C::NB - LOOK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerOp, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, LOOK, 0);
-    }
-    pv(pop, b);
-    interleave_reads_with_mfma<C::PV_STEPS * C::MB, kReadsPerOp, LOOK>();
-    if (more) store_k(b ^ 1);
-    if (kNext) store_v(b ^ 1);
-    __syncthreads();
-  };
-
-  // prologue: K_0 -> stage 0, S_0; then stage 1 = {K_1, V_0}
-  load_k(0);
-  store_k(0);
-  __syncthreads();
-  if (T > 1) load_k(1);
-  load_v(0);
-  qk(sa, 0);
-  interleave_reads_with_mfma<C::QK_STEPS * C::NB, kReadsPerOp, LOOK>();
-  if (T > 1) store_k(1);
-  store_v(1);
-  __syncthreads();
-
-  int j = 0;
-  for (; j + 2 < T; j += 2) {
-    step(sa, sb, j, BoolTag<true>{});
-    step(sb, sa, j + 1, BoolTag<true>{});
-  }
-  if (T - j == 2) {
-    step(sa, sb, j, BoolTag<true>{});
-    step(sb, sa, j + 1, BoolTag<false>{});
-  } else {
-    step(sa, sb, j, BoolTag<false>{});
-  }
-
-  const float l_tot = swap_halves_sum(l_run);
-  const float inv = dv / l_tot;
-  if (my_q < N) {
-    if (hh == 0)
-      p.lse[(size_t)bh * N + my_q] =
-          (m_run - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
-    const size_t obase = ((size_t)bh * N + my_q) * D;
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = 32 * mb + 8 * jj + 4 * hh;
-        const float x0 = oacc[mb][4 * jj + 0] * inv, x1 = oacc[mb][4 * jj + 1] * inv;
-        const float x2 = oacc[mb][4 * jj + 2] * inv, x3 = oacc[mb][4 * jj + 3] * inv;
-        if constexpr (DT == kF32) {
-          *(float4*)((float*)p.o + obase + d0) = make_float4(x0, x1, x2, x3);
-        } else {
-          uint2 pk;
-          pk.x = pack_bf16(x0, x1);
-          pk.y = pack_bf16(x2, x3);
-          *(uint2*)((unsigned short*)p.o + obase + d0) = pk;
-        }
-      }
-  }
-}
-
-
-// ---------------------------------------------------------------------------
 // DMA variant (head dim 128, bf16 and fp8): K and V tiles go global -> LDS
 // with buffer_load ... lds (no registers, no LDS store instructions, no
 // repacking), row-major with a 16-byte XOR swizzle per row, and the V^T MFMA
