@@ -157,15 +157,23 @@ __host__ __device__ __forceinline__ constexpr int vt_pos(int key) {
 __device__ __forceinline__ void swap_halves(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// Maximum / minimum that propagate NaN (llvm.maximum / llvm.minimum): on gfx950
+// they map to v_maximum3_f32 / v_minimum3_f32 as they stand. fmaxf / fminf
+// (IEEE maxNum) would make the compiler quiet every MFMA output with an extra
+// v_max_f32 first, doubling the cost of a row maximum. Scores are never NaN for
+// finite inputs (masked ones are -inf), so the two agree on every valid input.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
 __device__ __forceinline__ float swap_halves_max(float x) {
   float a = x, b = x;
   swap_halves(a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float swap_halves_min(float x) {
   float a = x, b = x;
   swap_halves(a, b);
-  return fminf(a, b);
+  return vmin(a, b);
 }
 __device__ __forceinline__ float swap_halves_sum(float x) {
   float a = x, b = x;
@@ -221,20 +229,20 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
 }
 
 // Max of n values (n a multiple of 8) as four interleaved chains of
-// three-input maxima (v_max3_f32): about n/2 instructions, short chains.
+// three-input maxima (v_maximum3_f32): about n/2 instructions, short chains.
 template <int NV, typename Get>
 __device__ __forceinline__ float max_reduce(Get get) {
   static_assert(NV % 8 == 0, "max_reduce takes a multiple of 8 values");
-  float m0 = fmaxf(get(0), get(1)), m1 = fmaxf(get(2), get(3));
-  float m2 = fmaxf(get(4), get(5)), m3 = fmaxf(get(6), get(7));
+  float m0 = vmax(get(0), get(1)), m1 = vmax(get(2), get(3));
+  float m2 = vmax(get(4), get(5)), m3 = vmax(get(6), get(7));
 #pragma unroll
   for (int i = 8; i < NV; i += 8) {
-    m0 = fmaxf(fmaxf(m0, get(i + 0)), get(i + 1));
-    m1 = fmaxf(fmaxf(m1, get(i + 2)), get(i + 3));
-    m2 = fmaxf(fmaxf(m2, get(i + 4)), get(i + 5));
-    m3 = fmaxf(fmaxf(m3, get(i + 6)), get(i + 7));
+    m0 = vmax(vmax(m0, get(i + 0)), get(i + 1));
+    m1 = vmax(vmax(m1, get(i + 2)), get(i + 3));
+    m2 = vmax(vmax(m2, get(i + 4)), get(i + 5));
+    m3 = vmax(vmax(m3, get(i + 6)), get(i + 7));
   }
-  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  return vmax(vmax(m0, m1), vmax(m2, m3));
 }
 
 // Buffer resource over [base, base + bytes): loads at offsets >= bytes return
@@ -513,7 +521,7 @@ fa_fwd_kernel(FwdArgs p) {
       // O needs no rescale. l and O always share the reference, so the result
       // is unchanged.
       const float m_tile = ext * c;
-      const float m_new = m_tile > m_run + kTau ? fmaxf(m_run, m_tile) : m_run;
+      const float m_new = m_tile > m_run + kTau ? vmax(m_run, m_tile) : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       const float m_sub = m_new - kPBias;
@@ -636,6 +644,35 @@ __device__ __forceinline__ int swz_v(int dt_fp8, int row) {
   return dt_fp8 ? ((row & 3) | (((row >> 3) & 1) << 2)) : 2 * (row & 3);
 }
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// One LDS DMA instruction: lane L's 16 bytes at byte voff of the buffer
+// [base, base + bytes) (zeros past its end) land at LDS address lds + 16 L.
+// Written as inline asm on purpose: the compiler tracks a buffer_load ... lds
+// it emits itself as an LDS write and, unable to tell the stages of the ring
+// apart, waits for every DMA in flight (vmcnt(0)) before the next LDS read,
+// i.e. for the prefetch of a later tile before the current one is used. Hidden
+// from it, the DMAs are ordered only by the kernel's own wait_vmcnt + barrier
+// (extra VMEM operations the compiler does not know of can only make its own
+// vmcnt waits stricter). base, bytes and lds must be wave-uniform. The s_nop
+// covers the SALU M0 write -> LDS DMA and VALU SGPR write -> VMEM read waits.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, uint32_t lds, uint32_t voff) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
@@ -675,7 +712,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
   static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three stages");
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
@@ -752,11 +789,10 @@ fa_fwd_dma_kernel(FwdArgs p) {
       const int r0 = kbase + t * T_ROWS;
       const int rem_rows = N - r0;
       const uint32_t bytes = rem_rows > 0 ? (uint32_t)rem_rows * ROW : 0u;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (size_t)(r0 > N ? N : r0) * ROW, bytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (size_t)(r0 > N ? N : r0) * ROW, bytes);
-      const int off = 1024 * (wave + NWAVES * t);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(st + off), 16, k_goff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(st + TILE + off), 16, v_goff, 0, 0, 0);
+      const size_t g0 = (size_t)(r0 > N ? N : r0) * ROW;
+      const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_ptr)(st + 1024 * (wave + NWAVES * t));
+      lds_dma16(Kg + g0, bytes, lds, k_goff);
+      lds_dma16(Vg + g0, bytes, lds + TILE, v_goff);
     }
   };
 
@@ -797,18 +833,14 @@ fa_fwd_dma_kernel(FwdArgs p) {
   constexpr float masked_raw = -__builtin_inff();
   constexpr int kReadsPerOp = Op::DW / 4;
 
-  // every wave issues 2 NINSTR DMA loads per tile
+  // every wave issues 2 NINSTR DMA loads per tile. The prologue waits for all
+  // of its loads (Q included): the compiler's own vmcnt bookkeeping, blind to
+  // the DMAs, then has nothing pending inside the loop.
   issue_tile(0, 0);
   if constexpr (NSTAGE == 3) {
-    if (T > 1) {
-      issue_tile(1, 1);
-      wait_vmcnt<2 * NINSTR>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  } else {
-    wait_vmcnt<0>();
+    if (T > 1) issue_tile(1, 1);
   }
+  wait_vmcnt<0>();
   __syncthreads();
 
   int buf = 0;   // stage of tile j
@@ -862,18 +894,17 @@ fa_fwd_dma_kernel(FwdArgs p) {
           }
       }
       const float ext = swap_halves_max(max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; }));
-      const float m_new = fmaxf(m_run, ext * c);
+      const float m_new = vmax(m_run, ext * c);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       const float m_sub = m_new - kPBias;
-      float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
-          ps[r & 3] += s[b][r];
-        }
+        for (int r = 0; r < 16; ++r) s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
+      float ps[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+      for (int i = 4; i < NB * 16; ++i) ps[i & 3] += s[i >> 4][i & 15];
       l_run = alpha * l_run + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
       if (__any(alpha != 1.0f)) {
 #pragma unroll
