@@ -29,6 +29,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -50,8 +52,13 @@ typedef enum {
   FA_ERR_SCALE = -5,     /* scale is NaN or infinite                            */
   FA_ERR_DESCALES = -6,  /* FP8 requested without a descale array               */
   FA_ERR_ALIGN = -7,     /* a tensor pointer is not 16-byte aligned             */
-  FA_ERR_HIP = -8        /* the HIP runtime rejected a launch                   */
+  FA_ERR_HIP = -8,       /* the HIP runtime rejected a launch                   */
+  FA_ERR_WORKSPACE = -9, /* split-KV workspace NULL, misaligned or too small    */
+  FA_ERR_SPLITS = -10    /* num_splits / num_parts outside 1..FA_MAX_SPLITS     */
 } fa_status_t;
+
+/* Largest number of key chunks fa_fwd_splitkv and fa_merge_partials accept. */
+#define FA_MAX_SPLITS 64
 
 /*
  * fa_fwd -- the FlashAttention-2 forward pass.
@@ -102,6 +109,93 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* descale,
                     int B, int H, int N, int d, hipStream_t stream);
+
+/*
+ * Split-KV forward ("Kernels and Memory in LLM Inference", section
+ * "Flash-Decoding: one token, whole chip": cut the keys into contiguous
+ * chunks, give every chunk its own workgroup with its own running max and sum,
+ * and merge the partial results in a second kernel by rescaling each to the
+ * overall max). It multiplies the number of workgroups when B*H*ceil(N/128)
+ * alone cannot fill the device. The result is the same attention as fa_fwd,
+ * up to rounding.
+ */
+
+/*
+ * fa_splitkv_chunk_keys -- keys per chunk when the keys are cut into
+ * num_splits chunks: chunk = 128 * ceil(ceil(N / num_splits) / 128). Chunk s
+ * covers the keys [s * chunk, min(N, (s + 1) * chunk)); only the first
+ * ceil(N / chunk) <= num_splits chunks hold keys. Returns 0 when N <= 0 or
+ * num_splits is outside 1..FA_MAX_SPLITS.
+ */
+int fa_splitkv_chunk_keys(int N, int num_splits);
+
+/*
+ * fa_splitkv_workspace_bytes -- device workspace fa_fwd_splitkv needs:
+ * 4 * num_splits * B*H * N * (d + 1) bytes. Returns 0 for invalid arguments
+ * (negative sizes, d not 64 or 128, num_splits outside 1..FA_MAX_SPLITS).
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
+
+/*
+ * fa_splitkv_default_splits -- the num_splits this library picks for a shape
+ * on the current device: 1 when the B*H*ceil(N/128) workgroups of fa_fwd
+ * already fill every compute unit as many times as it holds workgroups at once
+ * (three for head dim 128 in bf16 / FP8, two otherwise); else the number of
+ * chunks that does, at most one chunk per 256 keys and at most 16. Always
+ * returns a value >= 1 (1 for invalid arguments or a failed device query).
+ */
+int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype);
+
+/*
+ * fa_fwd_splitkv -- the forward pass computed chunk by chunk, then merged.
+ *
+ *   q ... descales  as fa_fwd (same layouts, dtypes and validation).
+ *   num_splits      1..FA_MAX_SPLITS; chunks as fa_splitkv_chunk_keys.
+ *   workspace       device memory owned by the caller, 16-byte aligned, at
+ *                   least fa_splitkv_workspace_bytes(B, H, N, d, num_splits)
+ *                   bytes. After the call (stream-ordered) it holds the
+ *                   partial results of the written chunks s < ceil(N / chunk):
+ *                     o_parts   float [num_splits][B*H][N][d] from byte 0:
+ *                               chunk s's output divided by the chunk's own
+ *                               softmax sum (already multiplied by the V
+ *                               descale for FP8);
+ *                     lse_parts float [num_splits][B*H][N] right after
+ *                               o_parts: the chunk's natural-log logsumexp of
+ *                               the scaled scores, -inf for a row with no valid
+ *                               key in the chunk (its o_parts row is then 0).
+ *   workspace_bytes size of `workspace`, checked against the need.
+ *
+ * Enqueues two kernels: the chunked forward, then the merge of
+ * fa_merge_partials over the written chunks into o and lse. Calls sharing a
+ * workspace must not overlap.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, int dtype,
+                   const float* descales, int num_splits, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_merge_partials -- merge attention results computed over disjoint sets of
+ * keys (the second kernel of the same section). Per (batch*head, row):
+ *   M = max_s L_s,  w_s = exp(L_s - M),  O = sum_s w_s O_s / sum_s w_s,
+ *   L = M + log sum_s w_s;
+ * parts with L_s = -inf weigh nothing, and a row whose parts are all -inf gets
+ * O = 0 and L = -inf.
+ *
+ *   o_parts    float [num_parts][B*H][N][d], 16-byte aligned: each part's
+ *              output divided by its own softmax sum.
+ *   lse_parts  float [num_parts][B*H][N]: each part's natural-log logsumexp.
+ *   num_parts  1..FA_MAX_SPLITS.
+ *   d          64 or 128.
+ *   out_dtype  FA_DTYPE_F32 (float O) or FA_DTYPE_BF16 (bfloat16 O).
+ *   o          [B*H][N][d] output, 16-byte aligned; lse [B*H][N] output.
+ *
+ * Parts may come from anywhere (fa_fwd_splitkv's workspace, or the share of
+ * the keys another device holds) as long as they follow this layout.
+ */
+int fa_merge_partials(const float* o_parts, const float* lse_parts, int num_parts,
+                      int B, int H, int N, int d, int out_dtype, void* o, float* lse,
+                      hipStream_t stream);
 
 /* Human-readable name of a fa_status_t value. Never NULL. */
 const char* fa_status_string(int status);

@@ -36,7 +36,9 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_quantize_fp8", "fa_status_string"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8",
+                                     "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
+                                     "fa_splitkv_workspace_bytes", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -53,6 +55,8 @@ def test_binding_constants_match_header():
                   "FA_DTYPE_FP8_E4M3": fa.DTYPE_FP8_E4M3}
     st = {v: k for k, v in _header_enum("FA_").items() if not k.startswith("FA_DTYPE_")}
     assert st == fa.STATUS
+    m = re.search(r"#define\s+FA_MAX_SPLITS\s+(\d+)", _header_text())
+    assert m and int(m.group(1)) == fa.FA_MAX_SPLITS
 
 
 def test_status_strings(lib):
@@ -106,3 +110,68 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         fa.lib()
+
+
+# --------------------------------------------------------------------------
+# split-KV: host-side helpers and validation (nothing is launched)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("N,S,chunk", [
+    (4096, 1, 4096), (4096, 3, 1408), (4096, 4, 1024), (30272, 3, 10112),
+    (200, 4, 128), (1, 1, 128), (129, 2, 128), (0, 2, 0), (100, 0, 0), (100, 65, 0),
+])
+def test_chunk_keys(lib, N, S, chunk):
+    # 128 * ceil(ceil(N / S) / 128)
+    assert lib.fa_splitkv_chunk_keys(N, S) == chunk
+
+
+def test_workspace_bytes(lib):
+    assert fa.splitkv_workspace_bytes(1, 8, 4096, 128, 3) == 4 * 3 * 8 * 4096 * 129
+    assert fa.splitkv_workspace_bytes(2, 3, 100, 64, 5) == 4 * 5 * 6 * 100 * 65
+    assert fa.splitkv_workspace_bytes(1, 1, 100, 96, 2) == 0
+    assert fa.splitkv_workspace_bytes(1, 1, 100, 64, 0) == 0
+    assert fa.splitkv_workspace_bytes(-1, 1, 100, 64, 2) == 0
+
+
+def test_default_splits_is_at_least_one(lib):
+    for args in [(1, 8, 4096, 128, 0, 1), (1, 56, 30272, 128, 0, 1), (0, 1, 1, 64, 0, 0),
+                 (1, 1, 100, 96, 0, 1)]:
+        assert lib.fa_splitkv_default_splits(*args) >= 1
+
+
+WS = ctypes.c_void_p(0x40000)
+
+
+def _split(lib, num_splits=2, ws=WS, ws_bytes=1 << 40, **kw):
+    p = dict(q=A, k=A, v=A, o=A2, lse=A2, B=1, H=1, N=128, d=128, causal=0, scale=0.1, dtype=1,
+             descales=None)
+    p.update(kw)
+    return lib.fa_fwd_splitkv(p["q"], p["k"], p["v"], p["o"], p["lse"], p["B"], p["H"], p["N"],
+                              p["d"], p["causal"], p["scale"], p["dtype"], p["descales"], num_splits,
+                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(dtype=5), -3), (dict(d=32), -4), (dict(scale=float("nan")), -5),
+    (dict(dtype=2), -6), (dict(q=None), -1), (dict(k=MIS), -7),
+    (dict(num_splits=0), -10), (dict(num_splits=65), -10), (dict(num_splits=-2), -10),
+    (dict(ws=None), -9), (dict(ws=ctypes.c_void_p(0x40004)), -9),
+    (dict(ws_bytes=4 * 2 * 128 * 129 - 1), -9),
+    (dict(N=0), 0), (dict(H=0), 0),
+])
+def test_splitkv_validation_codes(lib, kw, code):
+    assert _split(lib, **kw) == code
+
+
+def _merge(lib, op=A, lp=A2, S=2, B=1, H=1, N=16, d=128, out_dtype=1, o=WS, lse=A2):
+    return lib.fa_merge_partials(op, lp, S, B, H, N, d, out_dtype, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(out_dtype=2), -3), (dict(out_dtype=9), -3), (dict(d=96), -4),
+    (dict(S=0), -10), (dict(S=65), -10),
+    (dict(op=None), -1), (dict(lp=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(op=MIS), -7), (dict(o=MIS), -7),
+    (dict(N=0), 0), (dict(B=0), 0),
+])
+def test_merge_validation_codes(lib, kw, code):
+    assert _merge(lib, **kw) == code

@@ -1,4 +1,5 @@
-"""Parity of the HIP forward (through the C ABI) with the fp64 CPU oracle.
+"""Parity of the HIP forward (fa_fwd, through the C ABI) with the fp64 CPU oracle.
+The split-KV path has its own tests.
 
 Tolerances (max-abs over the compared elements):
   O: 1e-5 (fp32), 1e-2 (bf16), 6e-2 (fp8, plus cosine >= 0.999 with the
@@ -51,12 +52,12 @@ def _run(q, k, v, dtype, causal, scale):
         c_v, ds_v = oracle.quantize_per_head(v)
         descales = torch.from_numpy(np.stack([ds_q.ravel(), ds_k.ravel(), ds_v.ravel()])).cuda()
         qd, kd, vd = _dev(torch.from_numpy(c_q), torch.from_numpy(c_k), torch.from_numpy(c_v))
-        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, descales=descales)
+        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, descales=descales, num_splits=1)
         ref_in = (oracle.dequantize_per_head(c_q, ds_q), oracle.dequantize_per_head(c_k, ds_k),
                   oracle.dequantize_per_head(c_v, ds_v))
     else:
         qd, kd, vd = _dev(q, k, v)
-        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+        o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, num_splits=1)
         ref_in = (q, k, v)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ref_in

@@ -7,6 +7,7 @@
 
 #include "fa.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_merge_kernel.hpp"
 #include "fa_quant_kernel.hpp"
 
 namespace {
@@ -21,35 +22,120 @@ constexpr int kWavesPerSimd = 2;
 // transpose reads (the shapes the DiT benchmark runs). bf16: key tile 32,
 // three stages, three waves per SIMD; fp8: key tile 64, two stages, three
 // waves per SIMD.
-template <int DT>
-int launch_fwd_dma(fa::FwdArgs a, bool causal, hipStream_t stream) {
+template <int DT, bool CAUSAL, bool SPLIT>
+void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
   constexpr int BN = DT == fa::kBF16 ? 32 : 64;
   constexpr int NSTAGE = DT == fa::kBF16 ? 3 : 2;
   constexpr int LOOK = 2, WPE = 3;
-  const dim3 grid((unsigned)((long long)a.BH * a.n_qtiles));
-  const dim3 block(64 * kWaves);
+  const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
+  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT>),
+                     dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
+}
+
+template <int DT>
+int launch_fwd_dma(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
   if (causal)
-    hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, true, LOOK, WPE, NSTAGE>), grid, block, 0,
-                       stream, a);
+    split ? launch_fwd_dma_inst<DT, true, true>(a, stream) : launch_fwd_dma_inst<DT, true, false>(a, stream);
   else
-    hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, false, LOOK, WPE, NSTAGE>), grid, block, 0,
-                       stream, a);
+    split ? launch_fwd_dma_inst<DT, false, true>(a, stream) : launch_fwd_dma_inst<DT, false, false>(a, stream);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int DT, int D, int BN, bool CAUSAL, bool SPLIT>
+void launch_fwd_inst(const fa::FwdArgs& a, hipStream_t stream) {
+  using C = fa::Cfg<DT, D, BN, kWaves>;
+  const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
+  hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, CAUSAL, kWavesPerSimd, 0, SPLIT>),
+                     dim3((unsigned)items), dim3(C::NT), 0, stream, a);
 }
 
 template <int DT, int D, int BN>
-int launch_fwd(const fa::FwdArgs& a, bool causal, hipStream_t stream) {
-  using C = fa::Cfg<DT, D, BN, kWaves>;
-  const dim3 grid((unsigned)((long long)a.BH * a.n_qtiles));
-  const dim3 block(C::NT);
+int launch_fwd(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
   if (causal)
-    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, true, kWavesPerSimd>), grid, block, 0, stream, a);
+    split ? launch_fwd_inst<DT, D, BN, true, true>(a, stream) : launch_fwd_inst<DT, D, BN, true, false>(a, stream);
   else
-    hipLaunchKernelGGL((fa::fa_fwd_kernel<DT, D, BN, kWaves, false, kWavesPerSimd>), grid, block, 0, stream, a);
+    split ? launch_fwd_inst<DT, D, BN, false, true>(a, stream) : launch_fwd_inst<DT, D, BN, false, false>(a, stream);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Kernel choice by dtype and head dim (validated by the caller).
+int launch_any(const fa::FwdArgs& a, int dtype, int d, bool split, hipStream_t stream) {
+  const bool c = a.causal != 0;
+  switch (dtype) {
+    case FA_DTYPE_BF16:
+      return d == 128 ? launch_fwd_dma<fa::kBF16>(a, c, split, stream)
+                      : launch_fwd<fa::kBF16, 64, 64>(a, c, split, stream);
+    case FA_DTYPE_FP8_E4M3:
+      return d == 128 ? launch_fwd_dma<fa::kFP8>(a, c, split, stream)
+                      : launch_fwd<fa::kFP8, 64, 64>(a, c, split, stream);
+    default:
+      return d == 128 ? launch_fwd<fa::kF32, 128, 32>(a, c, split, stream)
+                      : launch_fwd<fa::kF32, 64, 32>(a, c, split, stream);
+  }
+}
+
+constexpr int kBM = 32 * kWaves;   // query rows per workgroup
+
+// Argument checks shared by fa_fwd and fa_fwd_splitkv, in the documented
+// order; fills the kernel arguments. Returns FA_OK with *empty = true when
+// there is nothing to compute.
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int N, int d, int causal, float scale, int dtype, const float* descales,
+                fa::FwdArgs& a, bool& empty);
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int N, int d, int causal, float scale, int dtype, const float* descales,
+                fa::FwdArgs& a, bool& empty) {
+  empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
+    return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (dtype == FA_DTYPE_FP8_E4M3 && descales == nullptr) return FA_ERR_DESCALES;
+  const long long BH = (long long)B * H;
+  if (BH == 0 || N == 0) {
+    empty = true;
+    return FA_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  const long long n_qtiles = ((long long)N + kBM - 1) / kBM;
+  if (BH > INT_MAX || BH * n_qtiles > INT_MAX) return FA_ERR_SHAPE;
+  // one head of Q, K or V is addressed with 32-bit buffer offsets
+  const long long es = dtype == FA_DTYPE_F32 ? 4 : dtype == FA_DTYPE_BF16 ? 2 : 1;
+  if (((long long)N + 128) * d * es > INT_MAX) return FA_ERR_SHAPE;
+
+  a = fa::FwdArgs{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.descales = descales;
+  a.BH = (int)BH;
+  a.N = N;
+  a.n_qtiles = (int)n_qtiles;
+  a.causal = causal ? 1 : 0;
+  a.scale = scale;
+  return FA_OK;
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, cached per device (0 if the query fails).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = cus;
+  return cus;
+}
 
 }  // namespace
 
@@ -64,6 +150,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_DESCALES: return "FA_ERR_DESCALES: FP8 needs a descale array";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV workspace missing, misaligned or too small";
+    case FA_ERR_SPLITS: return "FA_ERR_SPLITS: number of splits / parts must be 1..FA_MAX_SPLITS";
     default: return "unknown fa status";
   }
 }
@@ -71,47 +159,100 @@ extern "C" const char* fa_status_string(int status) {
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, int causal, float scale, int dtype,
                       const float* descales, hipStream_t stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
-    return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  if (!std::isfinite(scale)) return FA_ERR_SCALE;
-  if (dtype == FA_DTYPE_FP8_E4M3 && descales == nullptr) return FA_ERR_DESCALES;
-  const long long BH = (long long)B * H;
-  if (BH == 0 || N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
-  const int BM = 32 * kWaves;
-  const long long n_qtiles = ((long long)N + BM - 1) / BM;
-  if (BH > INT_MAX || BH * n_qtiles > INT_MAX) return FA_ERR_SHAPE;
-  // one head of Q, K or V is addressed with 32-bit buffer offsets
-  const long long es = dtype == FA_DTYPE_F32 ? 4 : dtype == FA_DTYPE_BF16 ? 2 : 1;
-  if (((long long)N + 128) * d * es > INT_MAX) return FA_ERR_SHAPE;
-
   fa::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.descales = descales;
-  a.BH = (int)BH;
-  a.N = N;
-  a.n_qtiles = (int)n_qtiles;
-  a.causal = causal ? 1 : 0;
-  a.scale = scale;
-  const bool c = causal != 0;
-  switch (dtype) {
-    case FA_DTYPE_BF16:
-      return d == 128 ? launch_fwd_dma<fa::kBF16>(a, c, stream)
-                      : launch_fwd<fa::kBF16, 64, 64>(a, c, stream);
-    case FA_DTYPE_FP8_E4M3:
-      return d == 128 ? launch_fwd_dma<fa::kFP8>(a, c, stream)
-                      : launch_fwd<fa::kFP8, 64, 64>(a, c, stream);
-    default:
-      return d == 128 ? launch_fwd<fa::kF32, 128, 32>(a, c, stream)
-                      : launch_fwd<fa::kF32, 64, 32>(a, c, stream);
+  bool empty = false;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, descales, a, empty);
+  if (st != FA_OK || empty) return st;
+  return launch_any(a, dtype, d, false, stream);
+}
+
+extern "C" int fa_splitkv_chunk_keys(int N, int num_splits) {
+  if (N <= 0 || num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
+  const long long per = ceil_div(N, num_splits);
+  return (int)(ceil_div(per, 128) * 128);
+}
+
+extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return 0;
+  return (size_t)4 * (size_t)num_splits * (size_t)B * (size_t)H * (size_t)N * (size_t)(d + 1);
+}
+
+extern "C" int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype) {
+  (void)causal;
+  if (B <= 0 || H <= 0 || N <= 0) return 1;
+  if (d != 64 && d != 128) return 1;
+  const int cus = device_cus();
+  if (cus <= 0) return 1;
+  const long long resident = (d == 128 && dtype != FA_DTYPE_F32) ? 3 : 2;
+  const long long slots = (long long)cus * resident;
+  const long long wgs = (long long)B * H * ceil_div(N, kBM);
+  if (wgs >= slots) return 1;
+  long long s = ceil_div(slots, wgs);
+  const long long by_keys = N / 256 > 1 ? N / 256 : 1;
+  if (s > by_keys) s = by_keys;
+  if (s > 16) s = 16;
+  return (int)(s < 1 ? 1 : s);
+}
+
+extern "C" int fa_merge_partials(const float* o_parts, const float* lse_parts, int num_parts,
+                                 int B, int H, int N, int d, int out_dtype, void* o, float* lse,
+                                 hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (out_dtype != FA_DTYPE_F32 && out_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (num_parts < 1 || num_parts > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  const long long rows = (long long)B * H * N;
+  if (rows == 0) return FA_OK;
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (!aligned16(o_parts) || !aligned16(o)) return FA_ERR_ALIGN;
+  const int rpb = 256 / (d / 4);
+  const long long blocks = ceil_div(rows, rpb);
+  if (blocks > INT_MAX) return FA_ERR_SHAPE;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (d == 128) {
+    if (out_dtype == FA_DTYPE_F32)
+      hipLaunchKernelGGL((fa::fa_merge_kernel<128, true>), grid, block, 0, stream, o_parts, lse_parts,
+                         num_parts, rows, o, lse);
+    else
+      hipLaunchKernelGGL((fa::fa_merge_kernel<128, false>), grid, block, 0, stream, o_parts, lse_parts,
+                         num_parts, rows, o, lse);
+  } else {
+    if (out_dtype == FA_DTYPE_F32)
+      hipLaunchKernelGGL((fa::fa_merge_kernel<64, true>), grid, block, 0, stream, o_parts, lse_parts,
+                         num_parts, rows, o, lse);
+    else
+      hipLaunchKernelGGL((fa::fa_merge_kernel<64, false>), grid, block, 0, stream, o_parts, lse_parts,
+                         num_parts, rows, o, lse);
   }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, int d, int causal, float scale, int dtype,
+                              const float* descales, int num_splits, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  fa::FwdArgs a;
+  bool empty = false;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, descales, a, empty);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (empty) return FA_OK;
+  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, num_splits);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const int chunk = fa_splitkv_chunk_keys(N, num_splits);
+  const int used = (int)ceil_div(N, chunk);               // chunks that hold keys
+  if ((long long)a.BH * a.n_qtiles * used > INT_MAX) return FA_ERR_SHAPE;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = o_parts + (size_t)num_splits * a.BH * (size_t)N * d;
+  a.n_splits = used;
+  a.split_keys = chunk;
+  a.o_part = o_parts;
+  a.lse_part = lse_parts;
+  const int r = launch_any(a, dtype, d, true, stream);
+  if (r != FA_OK) return r;
+  return fa_merge_partials(o_parts, lse_parts, used, B, H, N, d,
+                           dtype == FA_DTYPE_F32 ? FA_DTYPE_F32 : FA_DTYPE_BF16, o, lse, stream);
 }
 
 extern "C" int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* descale,

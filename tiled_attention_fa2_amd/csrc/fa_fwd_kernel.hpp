@@ -99,6 +99,13 @@ struct FwdArgs {
   int n_qtiles;
   int causal;
   float scale;
+  // Split-KV mode (kernels instantiated with SPLIT): split s of a query tile
+  // takes the keys [s * split_keys, (s + 1) * split_keys) and writes its
+  // partial result to o_part / lse_part instead of o / lse.
+  int n_splits;
+  int split_keys;     // a multiple of 128
+  float* o_part;      // [n_splits][BH][N][D] fp32
+  float* lse_part;    // [n_splits][BH][N] fp32
 };
 
 // Static shape of one instantiation.
@@ -197,6 +204,63 @@ __host__ __device__ __forceinline__ void work_item(int bid, int total, int n_qti
   qt = causal ? (n_qtiles - 1 - t) : t;
 }
 
+// Work item of a workgroup and its key-tile range [j_begin, j_end) out of the
+// n_ktiles tiles its query tile needs. Split-KV: the split index runs fastest
+// within a query tile, and split s takes the tiles holding the keys
+// [s * split_keys, (s + 1) * split_keys) ("Kernels and Memory in LLM
+// Inference", section "Flash-Decoding: one token, whole chip": the keys are cut
+// into chunks, one workgroup per chunk).
+template <bool SPLIT, int BN>
+__device__ __forceinline__ void split_item(const FwdArgs& p, int causal, int& bh, int& qt, int& sp) {
+  if constexpr (SPLIT) {
+    int t;
+    work_item(blockIdx.x, p.BH * p.n_qtiles * p.n_splits, p.n_qtiles * p.n_splits, causal, bh, t);
+    qt = t / p.n_splits;
+    sp = t - qt * p.n_splits;
+  } else {
+    work_item(blockIdx.x, p.BH * p.n_qtiles, p.n_qtiles, causal, bh, qt);
+    sp = 0;
+  }
+}
+template <bool SPLIT, int BN>
+__device__ __forceinline__ void key_tile_range(const FwdArgs& p, int sp, int n_ktiles, int& j_begin,
+                                               int& j_end) {
+  if constexpr (SPLIT) {
+    const int per = p.split_keys / BN;
+    j_begin = sp * per;
+    j_end = j_begin + per < n_ktiles ? j_begin + per : n_ktiles;
+  } else {
+    j_begin = 0;
+    j_end = n_ktiles;
+  }
+}
+
+// Split-KV epilogue of one lane: the chunk's output divided by the chunk's own
+// sum, in fp32, and the chunk's natural-log logsumexp L = ln2 (m2 + log2 l)
+// (m2 = running max in log2 units, bias removed). A row with no valid key in
+// the chunk (l = 0) gets O = 0 and L = -inf.
+template <int MB>
+__device__ __forceinline__ void store_partial(const FwdArgs& p, int sp, int bh, int my_q, int hh,
+                                              const f32x16 (&oacc)[MB], float l_tot, float m2,
+                                              float dv) {
+  constexpr int D = 32 * MB;
+  if (my_q >= p.N) return;
+  const size_t prow = ((size_t)sp * p.BH + bh) * (size_t)p.N + my_q;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : dv / l_tot;
+  if (hh == 0)
+    p.lse_part[prow] = empty ? -__builtin_inff() : (m2 + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+  float* dst = p.o_part + prow * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * mb + 8 * jj + 4 * hh;
+      *(float4*)(dst + d0) = make_float4(oacc[mb][4 * jj + 0] * inv, oacc[mb][4 * jj + 1] * inv,
+                                         oacc[mb][4 * jj + 2] * inv, oacc[mb][4 * jj + 3] * inv);
+    }
+}
+
 // Pairwise reduction of n values (n a power of two): depth log2(n) instead of
 // a chain of n - 1 dependent operations.
 template <int NV, typename Get, typename Op2>
@@ -271,7 +335,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // two workgroups share a CU and one wave's softmax overlaps another's MFMAs.
 // LOOK > 0 pins the order of each run of MFMAs and their LDS operand reads,
 // with LOOK operands read ahead (0 leaves the order to the compiler).
-template <int DT, int D, int BN, int NWAVES, bool CAUSAL, int WPE, int LOOK = 0>
+template <int DT, int D, int BN, int NWAVES, bool CAUSAL, int WPE, int LOOK = 0, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_kernel(FwdArgs p) {
   using C = Cfg<DT, D, BN, NWAVES>;
@@ -286,8 +350,8 @@ fa_fwd_kernel(FwdArgs p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_qtiles, p.n_qtiles, CAUSAL ? 1 : 0, bh, qt);
+  int bh, qt, sp;
+  split_item<SPLIT, BN>(p, CAUSAL ? 1 : 0, bh, qt, sp);
   const int N = p.N;
   const int q0 = qt * C::BM;
   const int q0w = q0 + 32 * wave;
@@ -352,6 +416,8 @@ fa_fwd_kernel(FwdArgs p) {
     const int last = (q0 + C::BM - 1) / BN + 1;
     n_ktiles = n_ktiles < last ? n_ktiles : last;
   }
+  int j_begin, j_end;
+  key_tile_range<SPLIT, BN>(p, sp, n_ktiles, j_begin, j_end);
 
   // ---- per-lane constant offsets ----
   // K staging: chunk tid + it*NT of the tile -> row, 16-byte column
@@ -448,13 +514,15 @@ fa_fwd_kernel(FwdArgs p) {
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  load_tile(0);
-  store_tile(0);
+  if (j_begin < j_end) {
+    load_tile(j_begin);
+    store_tile(0);
+  }
   __syncthreads();
 
-  for (int j = 0; j < n_ktiles; ++j) {
-    const int buf = j & 1;
-    const bool has_next = j + 1 < n_ktiles;
+  for (int j = j_begin; j < j_end; ++j) {
+    const int buf = (j - j_begin) & 1;
+    const bool has_next = j + 1 < j_end;
     if (has_next) load_tile(j + 1);
 
     const int kbase = j * BN;
@@ -522,9 +590,13 @@ fa_fwd_kernel(FwdArgs p) {
       // is unchanged.
       const float m_tile = ext * c;
       const float m_new = m_tile > m_run + kTau ? vmax(m_run, m_tile) : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // a causal chunk can start above a row's diagonal: until the row meets a
+      // valid key its max stays -inf, and a zero reference keeps p = 0, alpha = 0
+      float m_ref = m_new;
+      if constexpr (SPLIT && CAUSAL) m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       m_run = m_new;
-      const float m_sub = m_new - kPBias;
+      const float m_sub = m_ref - kPBias;
 
       // p = exp2(s*c - m_ref) (times 256 for fp8)
 #pragma unroll
@@ -594,6 +666,10 @@ fa_fwd_kernel(FwdArgs p) {
 
   // ---- epilogue: full row sum, L, O / l, bounded stores ----
   const float l_tot = swap_halves_sum(l_run);
+  if constexpr (SPLIT) {
+    store_partial<C::MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_run - kPBias, dv);
+    return;
+  }
   const float inv = dv / l_tot;
   if (my_q < N) {
     if (hh == 0)
@@ -690,7 +766,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // NSTAGE LDS stages: tile j lives in stage j % NSTAGE and is fetched
 // NSTAGE - 1 tiles ahead. WPE = waves per SIMD the registers must allow.
-template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2>
+template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int D = 128;
@@ -717,8 +794,8 @@ fa_fwd_dma_kernel(FwdArgs p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_qtiles, p.n_qtiles, CAUSAL ? 1 : 0, bh, qt);
+  int bh, qt, sp;
+  split_item<SPLIT, BN>(p, CAUSAL ? 1 : 0, bh, qt, sp);
   const int N = p.N;
   const int q0 = qt * BM;
   const int q0w = q0 + 32 * wave;
@@ -768,6 +845,8 @@ fa_fwd_dma_kernel(FwdArgs p) {
     const int last = (q0 + BM - 1) / BN + 1;
     T = T < last ? T : last;
   }
+  int j_begin, j_end;
+  key_tile_range<SPLIT, BN>(p, sp, T, j_begin, j_end);
 
   // ---- DMA: instruction t of this wave fills LDS chunks 64 (wave + NWAVES t) + lane ----
   // row r = chunk / CPR, physical column chunk pc -> logical pc ^ f(r); rows of
@@ -836,17 +915,17 @@ fa_fwd_dma_kernel(FwdArgs p) {
   // every wave issues 2 NINSTR DMA loads per tile. The prologue waits for all
   // of its loads (Q included): the compiler's own vmcnt bookkeeping, blind to
   // the DMAs, then has nothing pending inside the loop.
-  issue_tile(0, 0);
+  if (j_begin < j_end) issue_tile(j_begin, 0);
   if constexpr (NSTAGE == 3) {
-    if (T > 1) issue_tile(1, 1);
+    if (j_begin + 1 < j_end) issue_tile(j_begin + 1, 1);
   }
   wait_vmcnt<0>();
   __syncthreads();
 
   int buf = 0;   // stage of tile j
-  for (int j = 0; j < T; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int ahead = j + NSTAGE - 1;
-    if (ahead < T) {
+    if (ahead < j_end) {
       int nb = buf + NSTAGE - 1;
       nb = nb >= NSTAGE ? nb - NSTAGE : nb;
       issue_tile(ahead, nb);
@@ -895,9 +974,13 @@ fa_fwd_dma_kernel(FwdArgs p) {
       }
       const float ext = swap_halves_max(max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; }));
       const float m_new = vmax(m_run, ext * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      // a causal chunk can start above a row's diagonal: until the row meets a
+      // valid key its max stays -inf, and a zero reference keeps p = 0, alpha = 0
+      float m_ref = m_new;
+      if constexpr (SPLIT && CAUSAL) m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       m_run = m_new;
-      const float m_sub = m_new - kPBias;
+      const float m_sub = m_ref - kPBias;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -961,7 +1044,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
     }
     // tile j+1 must have landed; with three stages tile j+2 may stay in flight
     if constexpr (NSTAGE == 3) {
-      if (j + 2 < T)
+      if (j + 2 < j_end)
         wait_vmcnt<2 * NINSTR>();
       else
         wait_vmcnt<0>();
@@ -973,6 +1056,10 @@ fa_fwd_dma_kernel(FwdArgs p) {
   }
 
   const float l_tot = swap_halves_sum(l_run);
+  if constexpr (SPLIT) {
+    store_partial<MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_run - kPBias, dv);
+    return;
+  }
   const float inv = dv / l_tot;
   if (my_q < N) {
     if (hh == 0)

@@ -22,7 +22,8 @@ DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
           -4: "FA_ERR_HEAD_DIM", -5: "FA_ERR_SCALE", -6: "FA_ERR_DESCALES",
-          -7: "FA_ERR_ALIGN", -8: "FA_ERR_HIP"}
+          -7: "FA_ERR_ALIGN", -8: "FA_ERR_HIP", -9: "FA_ERR_WORKSPACE", -10: "FA_ERR_SPLITS"}
+FA_MAX_SPLITS = 64
 
 _lib = None
 
@@ -48,6 +49,17 @@ def lib() -> ctypes.CDLL:
         L.fa_quantize_fp8.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
+        sz = ctypes.c_size_t
+        L.fa_splitkv_chunk_keys.argtypes = [i, i]
+        L.fa_splitkv_chunk_keys.restype = i
+        L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_splitkv_workspace_bytes.restype = sz
+        L.fa_splitkv_default_splits.argtypes = [i, i, i, i, i, i]
+        L.fa_splitkv_default_splits.restype = i
+        L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        L.fa_fwd_splitkv.restype = i
+        L.fa_merge_partials.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, vp]
+        L.fa_merge_partials.restype = i
         _lib = L
     return _lib
 
@@ -86,13 +98,34 @@ def _check_qkv(q, k, v):
         raise ValueError("q, k and v must share a dtype")
 
 
+def splitkv_chunk_keys(N: int, num_splits: int) -> int:
+    """Keys per chunk of the split-KV forward (0 for invalid arguments)."""
+    return int(lib().fa_splitkv_chunk_keys(int(N), int(num_splits)))
+
+
+def splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> int:
+    """Device workspace bytes fa_fwd_splitkv needs (0 for invalid arguments)."""
+    return int(lib().fa_splitkv_workspace_bytes(int(B), int(H), int(N), int(d), int(num_splits)))
+
+
+def default_splits(B: int, H: int, N: int, d: int, causal: bool, dtype_code: int) -> int:
+    """The number of key chunks the library picks for this shape on the current device."""
+    return int(lib().fa_splitkv_default_splits(int(B), int(H), int(N), int(d),
+                                               1 if causal else 0, int(dtype_code)))
+
+
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None,
-        out=None, lse=None):
+        out=None, lse=None, num_splits: int | None = None, workspace=None):
     """FlashAttention-2 forward. q, k, v: contiguous [B, H, N, d] device
     tensors, all float32, all bfloat16, or all FP8 codes (uint8 or
     float8_e4m3fn) with descales [3, B*H] float32. Returns (o, lse):
     o [B, H, N, d] (float32 for float32 inputs, bfloat16 otherwise) and
-    lse [B, H, N] float32."""
+    lse [B, H, N] float32.
+
+    num_splits: None lets the library choose (fa_splitkv_default_splits);
+    1 runs fa_fwd; more runs fa_fwd_splitkv with that many key chunks, in
+    `workspace` (a uint8 device tensor of at least splitkv_workspace_bytes
+    bytes) or in one allocated here."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     code = _dtype_code(q)
@@ -113,11 +146,61 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
         if descales.dtype != torch.float32 or descales.numel() != 3 * B * H \
                 or not descales.is_contiguous() or not descales.is_cuda:
             raise ValueError("descales must be a contiguous float32 device tensor of 3*B*H values")
-    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                      1 if causal else 0, float(scale), code,
-                      _ptr(descales) if code == DTYPE_FP8_E4M3 else None, _stream())
+    ds = _ptr(descales) if code == DTYPE_FP8_E4M3 else None
+    if num_splits is None:
+        num_splits = default_splits(B, H, N, d, causal, code)
+    if num_splits == 1 and workspace is None:
+        st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                          1 if causal else 0, float(scale), code, ds, _stream())
+        if st != FA_OK:
+            raise FAError(st, "fa_fwd")
+        return out, lse
+    need = splitkv_workspace_bytes(B, H, N, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    st = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                              1 if causal else 0, float(scale), code, ds, int(num_splits),
+                              _ptr(workspace), workspace.numel(), _stream())
     if st != FA_OK:
-        raise FAError(st, "fa_fwd")
+        raise FAError(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def splitkv_partials(workspace, num_splits: int, B: int, H: int, N: int, d: int):
+    """Views of the partial results fa_fwd_splitkv leaves in its workspace:
+    (o_parts float32 [num_splits, B*H, N, d], lse_parts float32 [num_splits, B*H, N])."""
+    n_o = num_splits * B * H * N * d
+    f = workspace.view(torch.float32)
+    return (f[:n_o].view(num_splits, B * H, N, d),
+            f[n_o:n_o + num_splits * B * H * N].view(num_splits, B * H, N))
+
+
+def merge_partials(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=None):
+    """Merge partial attention results over disjoint key sets.
+    o_parts float32 [S, B*H, N, d], lse_parts float32 [S, B*H, N] (contiguous,
+    on the device). Returns (o [B*H, N, d] of out_dtype float32 or bfloat16,
+    lse float32 [B*H, N])."""
+    if o_parts.dim() != 4 or lse_parts.dim() != 3:
+        raise ValueError("o_parts must be [S, B*H, N, d] and lse_parts [S, B*H, N]")
+    S, BH, N, d = o_parts.shape
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor")
+    if tuple(lse_parts.shape) != (S, BH, N):
+        raise ValueError("lse_parts shape does not match o_parts")
+    code = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((BH, N, d), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((BH, N), dtype=torch.float32, device=o_parts.device)
+    st = lib().fa_merge_partials(_ptr(o_parts), _ptr(lse_parts), S, 1, BH, N, d, code,
+                                 _ptr(out), _ptr(lse), _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_merge_partials")
     return out, lse
 
 

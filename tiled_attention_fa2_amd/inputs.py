@@ -102,3 +102,22 @@ def sample_rows(N: int, tile: int = 128, n_random: int = 64, seed: int = 12345):
     rows.update(range(last_tile_start, N))
     rows.update(int(r) for r in rng.integers(0, N, size=n_random))
     return np.array(sorted(r for r in rows if 0 <= r < N), dtype=np.int64)
+
+
+def make_partials(S: int, BH: int, N: int, d: int, seed: int = 0, p_empty: float = 0.3,
+                  spread: float = 10.0):
+    """Seeded stand-ins for S partial attention results over disjoint key sets:
+    o_parts float32 [S, BH, N, d] ~ N(0, 4), lse_parts float32 [S, BH, N] ~
+    N(0, spread^2). A fraction p_empty of the (part, row) entries is empty
+    (L = -inf, O = 0); rows 0..4 of the first head are empty in every part; the
+    second head's first part is shifted up by 500 (weights far apart)."""
+    g = torch.Generator().manual_seed(seed)
+    o = torch.randn((S, BH, N, d), generator=g, dtype=torch.float32) * 2.0
+    lse = torch.randn((S, BH, N), generator=g, dtype=torch.float32) * spread
+    empty = torch.rand((S, BH, N), generator=g) < p_empty
+    empty[:, 0, :5] = True
+    if BH > 1:
+        lse[0, 1] += 500.0
+    lse[empty] = float("-inf")
+    o[empty] = 0.0
+    return o, lse
