@@ -37,10 +37,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def kernel_name(w) -> str:
+def kernel_name(w, num_splits: int = 1) -> str:
     """The kernel fa_fwd launches for this workload (head dim 128 bf16 / fp8
-    use the DMA + transpose-read kernel)."""
-    return "fa_fwd_dma_kernel" if (w.d == 128 and w.dtype in ("bf16", "fp8")) else "fa_fwd_kernel"
+    use the DMA + transpose-read kernel); with key chunks, the merge follows."""
+    k = "fa_fwd_dma_kernel" if (w.d == 128 and w.dtype in ("bf16", "fp8")) else "fa_fwd_kernel"
+    return k + " + fa_merge_kernel" if num_splits > 1 else k
 
 
 def measured_traffic(workload: str):
@@ -59,6 +60,11 @@ def measured_traffic(workload: str):
 def time_fwd(fa, torch, args_in, kw, steps, warmup):
     """Warm up, then time exactly `steps` launches. Returns (region ms per
     step, mean kernel ms from per-launch events)."""
+    splits = kw.get("num_splits") or 1
+    if splits > 1:   # the split-KV workspace, allocated once outside the timed region
+        B, H, N, d = args_in[0].shape
+        kw = dict(kw, workspace=torch.empty(fa.splitkv_workspace_bytes(B, H, N, d, splits),
+                                            dtype=torch.uint8, device=args_in[0].device))
     o, lse = fa.fwd(*args_in, **kw)
     kw = dict(kw, out=o, lse=lse)
     for _ in range(warmup):
@@ -123,6 +129,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="key chunks of the split-KV path (default: the library's choice; 1 = unsplit)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a kernel of known "
                          "traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -153,11 +161,13 @@ def main():
     q, k, v = make_qkv(w.B, w.H, w.N, w.d, "f32" if w.dtype == "f32" else "bf16", seed=0)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
 
+    code = {"f32": fa.DTYPE_F32, "bf16": fa.DTYPE_BF16, "fp8": fa.DTYPE_FP8_E4M3}[w.dtype]
+    splits = a.num_splits if a.num_splits is not None else fa.default_splits(w.B, w.H, w.N, w.d, w.causal, code)
     if w.dtype == "fp8":
         q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
-        main_in, main_kw = (q8, k8, v8), dict(causal=w.causal, scale=w.scale, descales=ds)
+        main_in, main_kw = (q8, k8, v8), dict(causal=w.causal, scale=w.scale, descales=ds, num_splits=splits)
     else:
-        main_in, main_kw = (qd, kd, vd), dict(causal=w.causal, scale=w.scale)
+        main_in, main_kw = (qd, kd, vd), dict(causal=w.causal, scale=w.scale, num_splits=splits)
     print("[bench] timing main leg", file=sys.stderr, flush=True)
     ms, kern_ms, wall_ms = time_fwd(fa, torch, main_in, main_kw, a.steps, a.warmup)
     flops = w.flops()
@@ -171,19 +181,24 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "pct_of_mfma_peak": round(100 * value / peak, 2),
+                   "causal": w.causal, "num_splits": splits,
+                   "pct_of_mfma_peak": round(100 * value / peak, 2),
                    "wall_ms_per_step": round(wall_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": kernel_name(w), "kernel_ms": round(kern_ms, 4)},
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic if splits == 1 else None,
+                     "kernel": kernel_name(w, splits), "kernel_ms": round(kern_ms, 4)},
     }
 
     if not a.no_fp8 and w.dtype == "bf16" and w.name.startswith("bf16_dit"):
         w8 = WORKLOADS["fp8_dit_b1_h56_n30272_d128"]
         print("[bench] timing fp8 leg", file=sys.stderr, flush=True)
         q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
+        splits8 = a.num_splits if a.num_splits is not None else fa.default_splits(
+            w8.B, w8.H, w8.N, w8.d, w8.causal, fa.DTYPE_FP8_E4M3)
         ms8, kern8, _ = time_fwd(fa, torch, (q8, k8, v8),
-                                 dict(causal=False, scale=w8.scale, descales=ds), a.steps, a.warmup)
+                                 dict(causal=False, scale=w8.scale, descales=ds, num_splits=splits8),
+                                 a.steps, a.warmup)
         # per-head quantise of Q, K and V (the FP8 path's first step), timed on its own
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -202,7 +217,8 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(w8.flops() / (kern8 * 1e-3) / 1e12, 2),
                          "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                          "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
-                         "traffic": measured_traffic(w8.name), "kernel": kernel_name(w8),
+                         "traffic": measured_traffic(w8.name) if splits8 == 1 else None,
+                         "kernel": kernel_name(w8, splits8),
                          "kernel_ms": round(kern8, 4)},
         }
 

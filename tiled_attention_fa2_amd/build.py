@@ -12,6 +12,7 @@ LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(PKG, "csrc", "fa_api.hip")]
 HEADERS = [os.path.join(ROOT, "include", "fa.h"),
            os.path.join(PKG, "csrc", "fa_fwd_kernel.hpp"),
+           os.path.join(PKG, "csrc", "fa_merge_kernel.hpp"),
            os.path.join(PKG, "csrc", "fa_quant_kernel.hpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -26,6 +27,8 @@ FLAGS = [
 
 PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
+CEILING_SRC = os.path.join(ROOT, "tests", "hip", "mfma_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_ceiling.so")
 
 
 def _hipcc(cmd, verbose):
@@ -38,9 +41,13 @@ def _hipcc(cmd, verbose):
 
 
 def build_probe(verbose: bool = False) -> str:
-    """The one-wave MFMA layout/precision probe used by the GPU tests."""
+    """The test helpers of tests/hip: the one-wave MFMA layout/precision probe
+    and the sustained-MFMA-rate probe used by the GPU tests."""
     _hipcc([HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_LIB + ".tmp"], verbose)
     os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    if os.path.exists(CEILING_SRC):
+        _hipcc([HIPCC, *FLAGS, CEILING_SRC, "-o", CEILING_LIB + ".tmp"], verbose)
+        os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
     return PROBE_LIB
 
 
