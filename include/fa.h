@@ -46,7 +46,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL                          */
-  FA_ERR_SHAPE = -2,     /* B, H or N negative                                  */
+  FA_ERR_SHAPE = -2,     /* B, H or N negative, heads not a multiple of KV heads, or too large */
   FA_ERR_DTYPE = -3,     /* unknown dtype code                                  */
   FA_ERR_HEAD_DIM = -4,  /* d is not 64 or 128                                  */
   FA_ERR_SCALE = -5,     /* scale is NaN or infinite                            */
@@ -196,6 +196,30 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 int fa_merge_partials(const float* o_parts, const float* lse_parts, int num_parts,
                       int B, int H, int N, int d, int out_dtype, void* o, float* lse,
                       hipStream_t stream);
+
+/*
+ * fa_fwd_gqa -- the forward pass with grouped-query attention ("Kernels and
+ * Memory in LLM Inference", section "Store less: MQA, GQA, MLA": the query
+ * heads are split into groups and each group shares one key head and one
+ * value head; Hkv = 1 is multi-query attention, Hkv = Hq ordinary multi-head
+ * attention). The groups are runs of consecutive query heads: query head h
+ * reads key/value head h / (Hq / Hkv).
+ *
+ *   q, o       [B, Hq, N, d];  lse [B, Hq, N]  (as fa_fwd with H = Hq).
+ *   k, v       [B, Hkv, N, d]; Hq must be a multiple of Hkv (else FA_ERR_SHAPE).
+ *   descales   FP8 only: device float [B*Hq + 2*B*Hkv]: q per query head, then
+ *              k, then v per key/value head (for Hkv = Hq this is fa_fwd's
+ *              [3][B*H]).
+ *   num_splits 1 runs the unsplit kernels (workspace ignored, may be NULL);
+ *              2..FA_MAX_SPLITS the split-KV path of fa_fwd_splitkv, with a
+ *              workspace of fa_splitkv_workspace_bytes(B, Hq, N, d, num_splits)
+ *              bytes laid out as there (partials per query head).
+ * Everything else as fa_fwd / fa_fwd_splitkv.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale, int dtype,
+               const float* descales, int num_splits, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
 
 /* Human-readable name of a fa_status_t value. Never NULL. */
 const char* fa_status_string(int status);

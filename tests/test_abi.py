@@ -36,7 +36,7 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8",
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_gqa", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8",
                                      "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
                                      "fa_splitkv_workspace_bytes", "fa_status_string"]
 
@@ -175,3 +175,23 @@ def _merge(lib, op=A, lp=A2, S=2, B=1, H=1, N=16, d=128, out_dtype=1, o=WS, lse=
 ])
 def test_merge_validation_codes(lib, kw, code):
     assert _merge(lib, **kw) == code
+
+
+def _gqa(lib, Hq=8, Hkv=2, num_splits=1, ws=None, ws_bytes=0, **kw):
+    p = dict(q=A, k=A, v=A, o=A2, lse=A2, B=1, N=128, d=128, causal=0, scale=0.1, dtype=1, descales=None)
+    p.update(kw)
+    return lib.fa_fwd_gqa(p["q"], p["k"], p["v"], p["o"], p["lse"], p["B"], Hq, Hkv, p["N"], p["d"],
+                          p["causal"], p["scale"], p["dtype"], p["descales"], num_splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), -2), (dict(Hkv=0), -2), (dict(Hkv=-2), -2), (dict(Hq=-1), -2), (dict(N=-3), -2),
+    (dict(dtype=4), -3), (dict(d=80), -4), (dict(scale=float("inf")), -5), (dict(dtype=2), -6),
+    (dict(v=None), -1), (dict(o=MIS), -7),
+    (dict(num_splits=0), -10), (dict(num_splits=65), -10),
+    (dict(num_splits=2), -9), (dict(num_splits=2, ws=ctypes.c_void_p(0x40008), ws_bytes=1 << 40), -9),
+    (dict(num_splits=3, ws=WS, ws_bytes=4 * 3 * 8 * 128 * 129 - 4), -9),
+    (dict(B=0), 0), (dict(N=0), 0), (dict(B=0, num_splits=4), 0),
+])
+def test_gqa_validation_codes(lib, kw, code):
+    assert _gqa(lib, **kw) == code

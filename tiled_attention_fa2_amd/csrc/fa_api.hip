@@ -80,16 +80,17 @@ constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 // order; fills the kernel arguments. Returns FA_OK with *empty = true when
 // there is nothing to compute.
 int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                int N, int d, int causal, float scale, int dtype, const float* descales,
+                int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
                 fa::FwdArgs& a, bool& empty);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                int N, int d, int causal, float scale, int dtype, const float* descales,
+                int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
                 fa::FwdArgs& a, bool& empty) {
   empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (H > 0 && (Hkv < 1 || H % Hkv != 0)) return FA_ERR_SHAPE;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
     return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -120,6 +121,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.n_qtiles = (int)n_qtiles;
   a.causal = causal ? 1 : 0;
   a.scale = scale;
+  a.group = H / Hkv;
   return FA_OK;
 }
 
@@ -156,14 +158,59 @@ extern "C" const char* fa_status_string(int status) {
   }
 }
 
+namespace {
+
+// The forward behind every entry point: Hq query heads over Hkv key/value
+// heads; num_splits == 0 runs the unsplit kernels (no workspace), >= 1 the
+// split-KV kernels and the merge in `workspace`.
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+            int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
+            int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::FwdArgs a;
+  bool empty = false;
+  const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, a, empty);
+  if (st != FA_OK) return st;
+  if (num_splits == 0) return empty ? FA_OK : launch_any(a, dtype, d, false, stream);
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (empty) return FA_OK;
+  const size_t need = fa_splitkv_workspace_bytes(B, Hq, N, d, num_splits);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const int chunk = fa_splitkv_chunk_keys(N, num_splits);
+  const int used = (int)ceil_div(N, chunk);               // chunks that hold keys
+  if ((long long)a.BH * a.n_qtiles * used > INT_MAX) return FA_ERR_SHAPE;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = o_parts + (size_t)num_splits * a.BH * (size_t)N * d;
+  a.n_splits = used;
+  a.split_keys = chunk;
+  a.o_part = o_parts;
+  a.lse_part = lse_parts;
+  const int r = launch_any(a, dtype, d, true, stream);
+  if (r != FA_OK) return r;
+  return fa_merge_partials(o_parts, lse_parts, used, B, Hq, N, d,
+                           dtype == FA_DTYPE_F32 ? FA_DTYPE_F32 : FA_DTYPE_BF16, o, lse, stream);
+}
+
+}  // namespace
+
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, int causal, float scale, int dtype,
                       const float* descales, hipStream_t stream) {
-  fa::FwdArgs a;
-  bool empty = false;
-  const int st = prepare_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, descales, a, empty);
-  if (st != FA_OK || empty) return st;
-  return launch_any(a, dtype, d, false, stream);
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, 0, nullptr, 0, stream);
+}
+
+extern "C" int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, int causal, float scale, int dtype,
+                          const float* descales, int num_splits, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) {
+    // shape and argument errors come first, as for the other entry points
+    fa::FwdArgs a;
+    bool empty = false;
+    const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, a, empty);
+    return st != FA_OK ? st : FA_ERR_SPLITS;
+  }
+  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales,
+                 num_splits == 1 ? 0 : num_splits, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa_splitkv_chunk_keys(int N, int num_splits) {
@@ -232,27 +279,9 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               int B, int H, int N, int d, int causal, float scale, int dtype,
                               const float* descales, int num_splits, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
-  fa::FwdArgs a;
-  bool empty = false;
-  const int st = prepare_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, descales, a, empty);
-  if (st != FA_OK) return st;
-  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
-  if (empty) return FA_OK;
-  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, num_splits);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  const int chunk = fa_splitkv_chunk_keys(N, num_splits);
-  const int used = (int)ceil_div(N, chunk);               // chunks that hold keys
-  if ((long long)a.BH * a.n_qtiles * used > INT_MAX) return FA_ERR_SHAPE;
-  float* o_parts = static_cast<float*>(workspace);
-  float* lse_parts = o_parts + (size_t)num_splits * a.BH * (size_t)N * d;
-  a.n_splits = used;
-  a.split_keys = chunk;
-  a.o_part = o_parts;
-  a.lse_part = lse_parts;
-  const int r = launch_any(a, dtype, d, true, stream);
-  if (r != FA_OK) return r;
-  return fa_merge_partials(o_parts, lse_parts, used, B, H, N, d,
-                           dtype == FA_DTYPE_F32 ? FA_DTYPE_F32 : FA_DTYPE_BF16, o, lse, stream);
+  if (num_splits == 0) num_splits = -1;   // 0 selects the unsplit path inside run_fwd
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, num_splits,
+                 workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* descale,

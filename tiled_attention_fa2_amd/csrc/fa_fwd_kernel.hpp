@@ -106,6 +106,12 @@ struct FwdArgs {
   int split_keys;     // a multiple of 128
   float* o_part;      // [n_splits][BH][N][D] fp32
   float* lse_part;    // [n_splits][BH][N] fp32
+  // Grouped-query attention ("Kernels and Memory in LLM Inference", section
+  // "Store less: MQA, GQA, MLA"): `group` consecutive query heads share one
+  // key/value head, so (batch*query head) bh reads K/V head bh / group of the
+  // BH / group key/value heads. group = 1 is ordinary multi-head attention.
+  // FP8 descales: q at [bh], k at [BH + bh / group], v at [BH + BH / group + bh / group].
+  int group;
 };
 
 // Static shape of one instantiation.
@@ -358,17 +364,19 @@ fa_fwd_kernel(FwdArgs p) {
   const int my_q = q0w + l32;
 
   const uint32_t head_bytes = (uint32_t)N * C::ROW;   // < 2^31, checked by the host
+  const int bkv = bh / p.group;                       // key/value head
   const size_t head_off = (size_t)bh * head_bytes;
+  const size_t kv_off = (size_t)bkv * head_bytes;
   const unsigned char* Qg = (const unsigned char*)p.q + head_off;
-  const unsigned char* Kg = (const unsigned char*)p.k + head_off;
-  const unsigned char* Vg = (const unsigned char*)p.v + head_off;
+  const unsigned char* Kg = (const unsigned char*)p.k + kv_off;
+  const unsigned char* Vg = (const unsigned char*)p.v + kv_off;
 
   // scale * log2(e), with the fp8 descales of Q and K folded in
   float c = p.scale * 1.4426950408889634f;
   float dv = 1.0f;
   if constexpr (DT == kFP8) {
-    c *= p.descales[bh] * p.descales[p.BH + bh];
-    dv = p.descales[2 * p.BH + bh];
+    c *= p.descales[bh] * p.descales[p.BH + bkv];
+    dv = p.descales[p.BH + p.BH / p.group + bkv];
   }
   // fp8 keeps P * 256 in e4m3's normal range ("1.8x Faster Attention on an
   // RTX 5080", section "P goes through shared memory"): exp2(t + 8) = 256 exp2(t),
@@ -802,16 +810,18 @@ fa_fwd_dma_kernel(FwdArgs p) {
   const int my_q = q0w + l32;
 
   const uint32_t head_bytes = (uint32_t)N * ROW;
+  const int bkv = bh / p.group;                       // key/value head
   const size_t head_off = (size_t)bh * head_bytes;
+  const size_t kv_off = (size_t)bkv * head_bytes;
   const unsigned char* Qg = (const unsigned char*)p.q + head_off;
-  const unsigned char* Kg = (const unsigned char*)p.k + head_off;
-  const unsigned char* Vg = (const unsigned char*)p.v + head_off;
+  const unsigned char* Kg = (const unsigned char*)p.k + kv_off;
+  const unsigned char* Vg = (const unsigned char*)p.v + kv_off;
 
   float c = p.scale * 1.4426950408889634f;
   float dv = 1.0f;
   if constexpr (DT == kFP8) {
-    c *= p.descales[bh] * p.descales[p.BH + bh];
-    dv = p.descales[2 * p.BH + bh];
+    c *= p.descales[bh] * p.descales[p.BH + bkv];
+    dv = p.descales[p.BH + p.BH / p.group + bkv];
   }
   constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
   // a negative scale is folded into Q (sign flip, exact), so c > 0 below

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_splitkv.restype = i
         L.fa_merge_partials.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, vp]
         L.fa_merge_partials.restype = i
+        L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
+        L.fa_fwd_gqa.restype = i
         _lib = L
     return _lib
 
@@ -92,8 +94,10 @@ def _check_qkv(q, k, v):
             raise ValueError(f"{name} must be a device tensor")
         if t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k and v must have the same [B, H, N, d] shape")
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2:] != k.shape[2:]:
+        raise ValueError("q must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    if k.shape[1] < 1 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("the query heads must be a multiple of the key/value heads")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share a dtype")
 
@@ -116,18 +120,22 @@ def default_splits(B: int, H: int, N: int, d: int, causal: bool, dtype_code: int
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None,
         out=None, lse=None, num_splits: int | None = None, workspace=None):
-    """FlashAttention-2 forward. q, k, v: contiguous [B, H, N, d] device
-    tensors, all float32, all bfloat16, or all FP8 codes (uint8 or
-    float8_e4m3fn) with descales [3, B*H] float32. Returns (o, lse):
-    o [B, H, N, d] (float32 for float32 inputs, bfloat16 otherwise) and
-    lse [B, H, N] float32.
+    """FlashAttention-2 forward. q: contiguous [B, Hq, N, d], k and v:
+    contiguous [B, Hkv, N, d] device tensors (Hq a multiple of Hkv: grouped-
+    query attention when Hkv < Hq), all float32, all bfloat16, or all FP8
+    codes (uint8 or float8_e4m3fn) with descales of B*Hq + 2*B*Hkv float32
+    values (q, k, v; [3, B*H] when Hkv == Hq). Returns (o, lse):
+    o [B, Hq, N, d] (float32 for float32 inputs, bfloat16 otherwise) and
+    lse [B, Hq, N] float32.
 
     num_splits: None lets the library choose (fa_splitkv_default_splits);
-    1 runs fa_fwd; more runs fa_fwd_splitkv with that many key chunks, in
-    `workspace` (a uint8 device tensor of at least splitkv_workspace_bytes
-    bytes) or in one allocated here."""
+    1 runs the unsplit kernels (fa_fwd, or fa_fwd_gqa for Hkv < Hq); more runs
+    the split-KV path with that many key chunks, in `workspace` (a uint8 device
+    tensor of at least splitkv_workspace_bytes bytes) or in one allocated
+    here."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -142,13 +150,25 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if code == DTYPE_FP8_E4M3:
         if descales is None:
-            raise ValueError("FP8 inputs need descales [3, B*H]")
-        if descales.dtype != torch.float32 or descales.numel() != 3 * B * H \
+            raise ValueError("FP8 inputs need descales (q, k, v per head)")
+        if descales.dtype != torch.float32 or descales.numel() != B * H + 2 * B * Hkv \
                 or not descales.is_contiguous() or not descales.is_cuda:
-            raise ValueError("descales must be a contiguous float32 device tensor of 3*B*H values")
+            raise ValueError("descales must be a contiguous float32 device tensor of "
+                             "B*Hq + 2*B*Hkv values")
     ds = _ptr(descales) if code == DTYPE_FP8_E4M3 else None
     if num_splits is None:
         num_splits = default_splits(B, H, N, d, causal, code)
+    if Hkv != H:
+        need = splitkv_workspace_bytes(B, H, N, d, num_splits) if num_splits > 1 else 0
+        if num_splits > 1 and workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        st = lib().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d,
+                              1 if causal else 0, float(scale), code, ds, int(num_splits),
+                              _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                              _stream())
+        if st != FA_OK:
+            raise FAError(st, "fa_fwd_gqa")
+        return out, lse
     if num_splits == 1 and workspace is None:
         st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                           1 if causal else 0, float(scale), code, ds, _stream())
@@ -228,10 +248,13 @@ def quantize_fp8(x, out=None, descale=None):
 
 
 def quantize_qkv_fp8(q, k, v):
-    """Quantise Q, K and V per head. Returns (q8, k8, v8, descales [3, B*H])."""
+    """Quantise Q, K and V per head. Returns (q8, k8, v8, descales): descales
+    [3, B*H] when Q, K and V have the same heads, else the flat
+    B*Hq + 2*B*Hkv layout fwd() takes for grouped-query attention."""
     B, H = q.shape[:2]
-    descales = torch.empty((3, B * H), dtype=torch.float32, device=q.device)
-    q8, _ = quantize_fp8(q, descale=descales[0])
-    k8, _ = quantize_fp8(k, descale=descales[1])
-    v8, _ = quantize_fp8(v, descale=descales[2])
-    return q8, k8, v8, descales
+    Hkv = k.shape[1]
+    flat = torch.empty(B * H + 2 * B * Hkv, dtype=torch.float32, device=q.device)
+    q8, _ = quantize_fp8(q, descale=flat[:B * H])
+    k8, _ = quantize_fp8(k, descale=flat[B * H:B * H + B * Hkv])
+    v8, _ = quantize_fp8(v, descale=flat[B * H + B * Hkv:])
+    return q8, k8, v8, (flat.view(3, B * H) if Hkv == H else flat)
