@@ -101,13 +101,15 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     qn = q.float().numpy()
     kn = k.float().numpy()
     vn = v.float().numpy()
+    group = w.H // w.kv_heads          # grouped-query attention: query head h reads K/V head h // group
     rows_done = 0
     t0 = time.perf_counter()
     h = 0
     r0 = 0
     while time.perf_counter() - t0 < budget_s:
         rows = np.arange(r0, min(r0 + 128, w.N))
-        oracle.attention(qn[:, h:h + 1], kn[:, h:h + 1], vn[:, h:h + 1], w.scale,
+        hk = h // group
+        oracle.attention(qn[:, h:h + 1], kn[:, hk:hk + 1], vn[:, hk:hk + 1], w.scale,
                          causal=w.causal, rows=rows)
         rows_done += len(rows)
         h = (h + 1) % w.H
@@ -143,7 +145,7 @@ def main():
     import torch
 
     from tiled_attention_fa2_amd import fa
-    from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv
+    from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv, make_workload
 
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
@@ -158,7 +160,10 @@ def main():
               file=sys.stderr, flush=True)
         del src, dst
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
-    q, k, v = make_qkv(w.B, w.H, w.N, w.d, "f32" if w.dtype == "f32" else "bf16", seed=0)
+    if w.dtype == "fp8":   # fp8 workloads quantise the bf16 draws on the device
+        q, k, v = make_qkv(w.B, w.H, w.N, w.d, "bf16", seed=0)
+    else:
+        _, (q, k, v) = make_workload(w.name, seed=0)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
 
     code = {"f32": fa.DTYPE_F32, "bf16": fa.DTYPE_BF16, "fp8": fa.DTYPE_FP8_E4M3}[w.dtype]
@@ -180,7 +185,7 @@ def main():
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "d": w.d,
                    "causal": w.causal, "num_splits": splits,
                    "pct_of_mfma_peak": round(100 * value / peak, 2),
                    "wall_ms_per_step": round(wall_ms, 4)},

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from tiled_attention_fa2_amd import fa
-from tiled_attention_fa2_amd.inputs import make_qkv
+from tiled_attention_fa2_amd.inputs import make_gqa, make_workload, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +30,7 @@ TOL_L = 1e-3
 
 
 def _gqa_inputs(B, Hq, Hkv, N, d, dtype, seed):
-    """Q with Hq heads and K, V with Hkv heads, from the seeded generator."""
-    q, _, _ = make_qkv(B, Hq, N, d, dtype, seed=seed)
-    _, k, v = make_qkv(B, Hkv, N, d, dtype, seed=seed + 1)
-    return q, k, v
+    return make_gqa(B, Hq, Hkv, N, d, dtype, seed=seed)
 
 
 def _device(q, k, v, dtype):
@@ -107,6 +104,22 @@ def test_gqa_quantiser_on_kv_heads_byte_exact():
         assert np.array_equal(t8.cpu().numpy(), codes)
         assert np.array_equal(ds[off:off + n].cpu().numpy(), scales.ravel().astype(np.float32))
         off += n
+
+
+def test_gqa_workload_sampled_rows():
+    # the benchmark's GQA workload (56 query heads over 8 K/V heads, 30272
+    # tokens) in the launch configuration bench.py times, on sampled rows
+    w, (q, k, v) = make_workload("bf16_gqa_b1_hq56_hkv8_n30272_d128", seed=0)
+    rows = sample_rows(w.N, tile=128, n_random=32)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_gqa(q, k, v, scale=w.scale, causal=w.causal, rows=rows)
+    got_o = o.float().cpu().double().numpy()[:, :, rows]
+    got_l = lse.cpu().double().numpy()[:, :, rows]
+    err_o = float(np.max(np.abs(got_o - O_ref)))
+    err_l = float(np.max(np.abs(got_l - L_ref)))
+    print(f"[case] {w.name}: max|dO|={err_o:.3e} max|dL|={err_l:.3e}", flush=True)
+    assert err_o <= TOL_O["bf16"] and err_l <= TOL_L
 
 
 def test_gqa_rejects_indivisible_heads():

@@ -27,6 +27,11 @@ class Workload:
     N: int
     d: int
     causal: bool
+    Hkv: int = 0        # key/value heads (grouped-query attention); 0 = H
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -46,6 +51,10 @@ WORKLOADS = {
         Workload("bf16_causal_b4_h32_n2048_d128", "bf16", 4, 32, 2048, 128, True),
         Workload("bf16_dit_b1_h56_n30272_d128", "bf16", 1, 56, 30272, 128, False),
         Workload("fp8_dit_b1_h56_n30272_d128", "fp8", 1, 56, 30272, 128, False),
+        # the DiT shape with grouped-query attention: 56 query heads over 8
+        # key/value heads ("Kernels and Memory in LLM Inference", section
+        # "Store less: MQA, GQA, MLA"; about 8 groups is the setting it names)
+        Workload("bf16_gqa_b1_hq56_hkv8_n30272_d128", "bf16", 1, 56, 30272, 128, False, Hkv=8),
     )
 }
 
@@ -86,8 +95,24 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def make_gqa(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0):
+    """Q with Hq heads, then K and V with Hkv heads: iid N(0,1) float32 from one
+    seeded generator in that order, rounded to bf16 unless dtype == "f32"."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    if dtype == "f32":
+        return q, k, v
+    if dtype in ("bf16", "fp8"):
+        return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
 def make_workload(name: str, seed: int = 0, variant: str = "iid"):
     w = WORKLOADS[name]
+    if w.kv_heads != w.H:
+        return w, make_gqa(w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, seed=seed)
     return w, make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed, variant=variant)
 
 
