@@ -1,0 +1,113 @@
+"""Parity of the HIP backward (fa_bwd, through the C ABI) with the fp64 oracle.
+
+The forward runs on the GPU first (its bf16 O and fp32 L are the backward's
+inputs, as in training); the oracle gets the same Q, K, V, dO and the same O
+(D = rowsum(dO * O) is formed from the O the caller holds) and computes
+dQ, dK, dV exactly. Tolerance per tensor (max-abs over all elements), from the
+arithmetic: the products take P and dS rounded to bf16 (relative 2^-9 each)
+and the outputs are bf16, so an error of a few 2^-9 of the tensor's largest
+magnitude plus the bf16 rounding floor of the exact answer; the test uses
+1e-2 * max|ref| + that floor, and cosine >= 0.9999.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tiled_attention_fa2_amd import fa
+from tiled_attention_fa2_amd.inputs import make_dout, make_gqa, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _floor(ref):
+    return float(np.max(np.abs(torch.from_numpy(ref).to(torch.bfloat16).double().numpy() - ref)))
+
+
+def _cos(a, b):
+    a, b = a.ravel(), b.ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def _check(q, k, v, do, causal, scale, label):
+    print(f"[case] {label} q={tuple(q.shape)} k={tuple(k.shape)} causal={causal} scale={scale}", flush=True)
+    qd, kd, vd, dod = (t.cuda().contiguous() for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, num_splits=1)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    group = q.shape[1] // k.shape[1]
+    kr = k.repeat_interleave(group, dim=1)
+    vr = v.repeat_interleave(group, dim=1)
+    dQ, dKr, dVr, _ = oracle.attention_backward(q, kr, vr, do, scale, causal=causal, o=o.cpu())
+    B, Hkv, N, d = k.shape
+    dK = dKr.reshape(B, Hkv, group, N, d).sum(axis=2)   # a shared K/V head sums its group's gradients
+    dV = dVr.reshape(B, Hkv, group, N, d).sum(axis=2)
+    for name, got, ref in (("dq", dq, dQ), ("dk", dk, dK), ("dv", dv, dV)):
+        g = got.float().cpu().double().numpy()
+        err = float(np.max(np.abs(g - ref)))
+        tol = 1e-2 * float(np.max(np.abs(ref))) + _floor(ref)
+        cos = _cos(g, ref)
+        print(f"    {name}: max|err|={err:.3e} tol={tol:.3e} max|ref|={np.max(np.abs(ref)):.3e} cos={cos:.7f}",
+              flush=True)
+        assert np.all(np.isfinite(g)), name
+        assert err <= tol, (label, name, err, tol)
+        if np.any(ref):
+            assert cos >= 0.9999, (label, name, cos)
+        else:   # an exactly zero gradient (one key: dS = 0) must come out exactly zero
+            assert not np.any(g), (label, name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_oracle(d, causal):
+    for B, H, N in [(1, 2, 300), (2, 1, 129), (1, 1, 1), (1, 2, 777)]:
+        q, k, v = make_qkv(B, H, N, d, "bf16", seed=N + d)
+        do = make_dout(B, H, N, d, seed=N + d + 1)
+        _check(q, k, v, do, causal, 1.0 / math.sqrt(d), label=f"N={N} d={d}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_gqa(causal):
+    q, k, v = make_gqa(1, 8, 2, 400, 128, "bf16", seed=3)
+    do = make_dout(1, 8, 400, 128, seed=4)
+    _check(q, k, v, do, causal, 1.0 / math.sqrt(128), label="gqa 8/2")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_backward_scale_values(scale):
+    q, k, v = make_qkv(1, 2, 260, 64, "bf16", seed=5)
+    do = make_dout(1, 2, 260, 64, seed=6)
+    for causal in (False, True):
+        _check(q, k, v, do, causal, scale, label=f"scale={scale}")
+
+
+def test_backward_stress_inputs():
+    for variant in ("peaked", "growing"):
+        q, k, v = make_qkv(1, 2, 512, 128, "bf16", seed=7, variant=variant)
+        do = make_dout(1, 2, 512, 128, seed=8)
+        for causal in (False, True):
+            _check(q, k, v, do, causal, 1.0 / math.sqrt(128), label=variant)
+
+
+def test_backward_deterministic():
+    q, k, v = (t.cuda() for t in make_qkv(1, 4, 1000, 128, "bf16", seed=9))
+    do = make_dout(1, 4, 1000, 128, seed=10).cuda()
+    o, lse = fa.fwd(q, k, v, causal=True, num_splits=1)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_rejects_bad_arguments():
+    q, k, v = (t.cuda() for t in make_qkv(1, 1, 64, 64, "bf16", seed=1))
+    o, lse = fa.fwd(q, k, v, num_splits=1)
+    do = torch.zeros_like(q)
+    with pytest.raises(TypeError):
+        fa.bwd(q.float(), k.float(), v.float(), o, lse, do)
+    small = torch.empty(8, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fa.FAError) as e:
+        fa.bwd(q, k, v, o, lse, do, workspace=small)
+    assert e.value.status == -9

@@ -1,0 +1,502 @@
+// FlashAttention-2 backward for gfx950 (MI355X): bf16, head dim 64 or 128.
+//
+// What it computes ("FlashAttention-2 from PyTorch to Triton", forward-pass
+// section and its list of what the first kernel leaves out; "Kernels and
+// Memory in LLM Inference", section "Training detour (brief)"): the forward
+// stored L = m + log l per row, so every tile of P is recomputed on chip as
+// P = exp(S - L) instead of being kept; with D = rowsum(dO * O) per row,
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// Three kernels:
+//   fa_bwd_pre_kernel    D per row and L in log2 units, into the workspace;
+//   fa_bwd_dkdv_kernel   one workgroup per (key/value head, 128 keys): every
+//                        wave keeps its 32 keys' K and V rows as MFMA
+//                        operands and its dK, dV accumulators, and streams the
+//                        query tiles (Q, dO and the (L, D) pairs) of every
+//                        query head of its group through LDS;
+//   fa_bwd_dq_kernel     one workgroup per (query head, 128 queries), the
+//                        "second pass" for dQ: every wave keeps its 32 query
+//                        rows of Q and dO and its dQ accumulator and streams
+//                        the K/V tiles, so no atomics are needed and the
+//                        result is deterministic.
+//
+// How it maps onto CDNA4 (the layouts of the forward kernel, roles swapped
+// where needed):
+//   * dK/dV kernel: S = Q K^T with A = Q rows from LDS and B = the wave's K
+//     rows; the 32x32 accumulator gives lane l key l%32 and 16 queries, so P
+//     and dS are B operands as they stand for dV^T += dO^T P and
+//     dK^T += Q^T dS, whose A operands (dO^T, Q^T) come from the Q / dO tiles
+//     with the LDS transpose read ds_read_b64_tr_b16, in the query order of
+//     the register slots (the forward's V^T read with keys and queries
+//     swapped). dP = dO V^T has the same layout as S.
+//   * dQ kernel: S^T = K Q^T and dP^T = V dO^T (A = K, V rows from LDS;
+//     B = the wave's Q, dO rows), P^T and dS^T per lane, and
+//     dQ^T += K^T dS^T with K^T read transposed from the K tile: the forward
+//     kernel with one more product and no running max (L is known).
+//   * Tiles go global -> LDS by DMA (buffer_load ... lds issued from inline
+//     asm, as in the forward), two stages, rows XOR-swizzled per 16-byte
+//     chunk with (row & 7); the transposed reads use the same swizzle.
+//   * Masking (keys or queries >= N, causal key > query) only on tiles that
+//     need it: masked scores give p = 0 whatever the sign of the scale.
+#pragma once
+
+#include "fa_fwd_kernel.hpp"
+
+namespace fa {
+
+struct BwdArgs {
+  const void* q;        // [BH][N][D] bf16
+  const void* k;        // [BH / group][N][D]
+  const void* v;        // [BH / group][N][D]
+  const void* o;        // [BH][N][D] forward output
+  const void* dout;     // [BH][N][D] upstream gradient dO
+  const float* lse;     // [BH][N] natural-log L of the forward
+  float2* ld;           // workspace [BH][N]: (L * log2 e, D)
+  void* dq;             // [BH][N][D] bf16 outputs
+  void* dk;             // [BH / group][N][D]
+  void* dv;             // [BH / group][N][D]
+  int BH;               // batch * query heads
+  int N;
+  int group;            // query heads per key/value head
+  int n_tiles;          // 128-row tiles per head
+  float scale;
+};
+
+// D = rowsum(dO * O) in fp32 and L in log2 units, one row per D/8 lanes.
+template <int D>
+__global__ void __launch_bounds__(256) fa_bwd_pre_kernel(BwdArgs p) {
+  constexpr int TPR = D / 8;          // lanes per row, 8 bf16 (16 bytes) each
+  constexpr int RPB = 256 / TPR;
+  const long long rows = (long long)p.BH * p.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)((const unsigned short*)p.o + row * D + 8 * c);
+    const u32x4 b = *(const u32x4*)((const unsigned short*)p.dout + row * D + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = a[i], y = b[i];
+      acc += u2f(x << 16) * u2f(y << 16);
+      acc += u2f(x & 0xffff0000u) * u2f(y & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) p.ld[row] = make_float2(p.lse[row] * 1.4426950408889634f, acc);
+}
+
+namespace bwd {
+
+constexpr int kNWaves = 4;
+constexpr int kRows = 32 * kNWaves;   // rows of the fixed side per workgroup
+
+// Shapes shared by both kernels: a streamed tile has 32 rows of D bf16.
+template <int D>
+struct Shape {
+  static constexpr int ES = 2, KPL = 8;
+  static constexpr int ROW = D * ES;                  // bytes per row
+  static constexpr int CPR = ROW / 16;                // 16-byte chunks per row
+  static constexpr int TILE = 32 * ROW;               // bytes per 32-row tile
+  static constexpr int NINSTR = TILE / 1024 / kNWaves;
+  static constexpr int T_ROWS = 64 * kNWaves / CPR;   // rows between DMA instructions
+  static constexpr int QK_STEPS = D / (2 * KPL);      // MFMAs over D
+  static constexpr int PV_STEPS = 32 / (2 * KPL);     // MFMAs over the 32 streamed rows
+  static constexpr int MB = D / 32;
+  static_assert(TILE % (1024 * kNWaves) == 0, "tile must split into whole DMA instructions");
+  static_assert(CPR >= 8, "swizzle needs at least 8 chunks per row");
+  static_assert(T_ROWS % 8 == 0, "swizzle period");
+};
+
+// Per-lane bases of the two LDS read patterns of a 32-row tile swizzled with
+// (row & 7): row-major A operands (lane = row, 16 bytes of k) and transposed
+// A operands (ds_read_b64_tr_b16: lane = feature, keys/queries in the order of
+// the 32x32 accumulator's register slots).
+template <int D>
+struct ReadBases {
+  uint32_t rm[4];   // row-major: read at rm[kk & 3] + 128 (kk >> 2)
+  uint32_t tr[2];   // transposed: read at tr[mb & 1] + 128 (mb >> 1) + (16 n + 8 t) ROW
+  __device__ __forceinline__ ReadBases(int lane) {
+    using S = Shape<D>;
+    const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rm[u] = (uint32_t)l32 * S::ROW + 16 * ((2 * u + hh) ^ (l32 & 7));
+    const int vg = lane >> 4, vj = lane & 15, va = vg & 1;
+    const int e = vj >> 2, q = vj & 3, r0 = 4 * hh + e, x = 2 * va + (q >> 1);
+#pragma unroll
+    for (int m1 = 0; m1 < 2; ++m1)
+      tr[m1] = (uint32_t)r0 * S::ROW + 16 * ((4 * m1 + x) ^ (r0 & 7)) + 8 * (q & 1);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void read_rm(const unsigned char* tile, const ReadBases<D>& rb, int kk,
+                                        Operand<kBF16>& a) {
+  const u32x4 w = *(const u32x4*)(tile + rb.rm[kk & 3] + 128 * (kk >> 2));
+#pragma unroll
+  for (int y = 0; y < 4; ++y) a.w[y] = w[y];
+}
+
+template <int D>
+__device__ __forceinline__ void read_tr(const unsigned char* tile, const ReadBases<D>& rb, int mb, int n,
+                                        Operand<kBF16>& a) {
+  using S = Shape<D>;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const unsigned char* src = tile + rb.tr[mb & 1] + 128 * (mb >> 1) + (16 * n + 8 * t) * S::ROW;
+    const s16x4_t v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)src);
+    const i32x2_t v2 = __builtin_bit_cast(i32x2_t, v4);
+    a.w[2 * t] = (uint32_t)v2[0];
+    a.w[2 * t + 1] = (uint32_t)v2[1];
+  }
+}
+
+// One 32-row tile of a [N][D] bf16 head (rows from r_first; rows >= N read as
+// zero) into LDS at `lds` by DMA: every wave issues NINSTR instructions.
+template <int D>
+__device__ __forceinline__ void dma_tile(const unsigned char* head, int N, int r_first, uint32_t lds,
+                                         int wave, uint32_t goff) {
+  using S = Shape<D>;
+#pragma unroll
+  for (int t = 0; t < S::NINSTR; ++t) {
+    const int r0 = r_first + t * S::T_ROWS;
+    const int rem = N - r0;
+    const uint32_t bytes = rem > 0 ? (uint32_t)rem * S::ROW : 0u;
+    lds_dma16(head + (size_t)(r0 > N ? N : r0) * S::ROW, bytes, lds + 1024 * (wave + kNWaves * t), goff);
+  }
+}
+
+// Packs 16 fp32 accumulator values of one lane into the bf16 B operands of
+// the PV-shaped products, in the slot order the transposed reads assume.
+__device__ __forceinline__ void pack_b(const float (&x)[16], Operand<kBF16> (&op)[2]) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) op[n].w[w] = pack_bf16(x[n * 8 + 2 * w], x[n * 8 + 2 * w + 1]);
+}
+
+// 32 rows x D of a lane's accumulators (lane = row l32, 16 values per 32
+// features) -> bf16 row `row` of `out`, times `mul`.
+template <int MB>
+__device__ __forceinline__ void store_rows(void* out, size_t row, int hh, const f32x16 (&acc)[MB],
+                                           float mul) {
+  constexpr int D = 32 * MB;
+  unsigned short* dst = (unsigned short*)out + row * D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 32 * mb + 8 * jj + 4 * hh;
+      uint2 pk;
+      pk.x = pack_bf16(acc[mb][4 * jj + 0] * mul, acc[mb][4 * jj + 1] * mul);
+      pk.y = pack_bf16(acc[mb][4 * jj + 2] * mul, acc[mb][4 * jj + 3] * mul);
+      *(uint2*)(dst + d0) = pk;
+    }
+}
+
+}  // namespace bwd
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (batch * query head, 128 queries); waves own 32 rows.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_bwd_dq_kernel(BwdArgs p) {
+  using S = bwd::Shape<D>;
+  using Op = Operand<kBF16>;
+  constexpr int QK = S::QK_STEPS, PV = S::PV_STEPS, MB = S::MB, ROW = S::ROW, TILE = S::TILE;
+  constexpr int STAGE = 2 * TILE;    // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  int bh, qt;
+  work_item(blockIdx.x, p.BH * p.n_tiles, p.n_tiles, CAUSAL ? 1 : 0, bh, qt);
+  const int N = p.N;
+  const int q0 = qt * bwd::kRows;
+  const int q0w = q0 + 32 * wave;
+  const int my_q = q0w + l32;
+  const uint32_t head_bytes = (uint32_t)N * ROW;
+  const int bkv = bh / p.group;
+  const unsigned char* Qg = (const unsigned char*)p.q + (size_t)bh * head_bytes;
+  const unsigned char* dOg = (const unsigned char*)p.dout + (size_t)bh * head_bytes;
+  const unsigned char* Kg = (const unsigned char*)p.k + (size_t)bkv * head_bytes;
+  const unsigned char* Vg = (const unsigned char*)p.v + (size_t)bkv * head_bytes;
+  const float c = p.scale * 1.4426950408889634f;
+
+  // the wave's Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T
+  Op qop[QK], dop[QK];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg, head_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dOg, head_bytes);
+    const uint32_t off = (uint32_t)my_q * ROW + hh * 16;
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rq, off + kk * 32, 0, 0);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rd, off + kk * 32, 0, 0);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        qop[kk].w[y] = a[y];
+        dop[kk].w[y] = b[y];
+      }
+    }
+  }
+  const float2 ld = my_q < N ? p.ld[(size_t)bh * N + my_q] : make_float2(0.0f, 0.0f);
+
+  int T = (N + 31) / 32;
+  if constexpr (CAUSAL) {
+    const int last = (q0 + bwd::kRows - 1) / 32 + 1;
+    T = T < last ? T : last;
+  }
+
+  const int dma_row = (64 * wave + lane) / S::CPR;
+  const int dma_pc = lane % S::CPR;
+  const uint32_t goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ (dma_row & 7));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_ptr)smem;
+  auto issue = [&](int jt, int buf) {
+    const uint32_t st = lds0 + buf * STAGE;
+    bwd::dma_tile<D>(Kg, N, jt * 32, st, wave, goff);
+    bwd::dma_tile<D>(Vg, N, jt * 32, st + TILE, wave, goff);
+  };
+  const bwd::ReadBases<D> rb(lane);
+
+  f32x16 dq[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[mb][r] = 0.0f;
+
+  issue(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int j = 0; j < T; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < T) issue(j + 1, buf ^ 1);
+    const int kbase = j * 32;
+    const bool wave_active = !CAUSAL || kbase <= q0w + 31;
+    if (wave_active) {
+      const unsigned char* st = smem + buf * STAGE;
+      f32x16 s, dpt;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.0f;
+        dpt[r] = 0.0f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < QK; ++kk) {
+        Op a, b;
+        bwd::read_rm<D>(st, rb, kk, a);
+        mfma<kBF16>(a, qop[kk], s);
+        bwd::read_rm<D>(st + TILE, rb, kk, b);
+        mfma<kBF16>(b, dop[kk], dpt);
+      }
+      // P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D); key kbase + 4hh + rel
+      const bool need_mask = (kbase + 32 > N) || (CAUSAL && kbase + 31 > q0w);
+      float ds[16];
+      if (need_mask) {
+        asm volatile("" ::: "memory");
+        int lim = N - kbase - 4 * hh;
+        if constexpr (CAUSAL) {
+          const int lim_c = my_q - kbase - 4 * hh + 1;
+          lim = lim < lim_c ? lim : lim_c;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = 8 * (r >> 2) + (r & 3);
+          const float t = rel < lim ? __builtin_fmaf(s[r], c, -ld.x) : -__builtin_inff();
+          const float pr = __builtin_amdgcn_exp2f(t);
+          ds[r] = pr * (dpt[r] - ld.y);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -ld.x));
+          ds[r] = pr * (dpt[r] - ld.y);
+        }
+      }
+      Op dsop[2];
+      bwd::pack_b(ds, dsop);
+      // dQ^T += K^T dS^T (K^T read transposed from the K tile)
+#pragma unroll
+      for (int n = 0; n < PV; ++n)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          Op a;
+          bwd::read_tr<D>(st, rb, mb, n, a);
+          mfma<kBF16>(a, dsop[n], dq[mb]);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  if (my_q < N) bwd::store_rows<MB>(p.dq, (size_t)bh * N + my_q, hh, dq, p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch * key/value head, 128 keys); waves own 32
+// keys and loop over the query tiles of every query head of their group.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dkdv_kernel(BwdArgs p) {
+  using S = bwd::Shape<D>;
+  using Op = Operand<kBF16>;
+  constexpr int QK = S::QK_STEPS, PV = S::PV_STEPS, MB = S::MB, ROW = S::ROW, TILE = S::TILE;
+  constexpr int STAGE = 2 * TILE + 1024;    // Q tile, dO tile, 32 (L2, D) pairs (1 KB slot)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+
+  const int BHkv = p.BH / p.group;
+  int bkv, kt;
+  work_item(blockIdx.x, BHkv * p.n_tiles, p.n_tiles, 0, bkv, kt);
+  const int N = p.N;
+  const int k0 = kt * bwd::kRows;
+  const int k0w = k0 + 32 * wave;
+  const int my_k = k0w + l32;
+  const uint32_t head_bytes = (uint32_t)N * ROW;
+  const unsigned char* Kg = (const unsigned char*)p.k + (size_t)bkv * head_bytes;
+  const unsigned char* Vg = (const unsigned char*)p.v + (size_t)bkv * head_bytes;
+  const float c = p.scale * 1.4426950408889634f;
+
+  // the wave's K and V rows: B operands of S = Q K^T and dP = dO V^T
+  Op kop[QK], vop[QK];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, head_bytes);
+    const uint32_t off = (uint32_t)my_k * ROW + hh * 16;
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk) {
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 32, 0, 0);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rv, off + kk * 32, 0, 0);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        kop[kk].w[y] = a[y];
+        vop[kk].w[y] = b[y];
+      }
+    }
+  }
+
+  const int dma_row = (64 * wave + lane) / S::CPR;
+  const int dma_pc = lane % S::CPR;
+  const uint32_t goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ (dma_row & 7));
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_ptr)smem;
+  const bwd::ReadBases<D> rb(lane);
+
+  f32x16 dk[MB], dv[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[mb][r] = 0.0f;
+      dv[mb][r] = 0.0f;
+    }
+
+  const int T = (N + 31) / 32;
+  // causal: queries before the workgroup's first key see none of its keys
+  const int j_first = CAUSAL ? k0 / 32 : 0;
+  for (int g = 0; g < p.group; ++g) {
+    const int bh = bkv * p.group + g;
+    const unsigned char* Qg = (const unsigned char*)p.q + (size_t)bh * head_bytes;
+    const unsigned char* dOg = (const unsigned char*)p.dout + (size_t)bh * head_bytes;
+    const float2* LDg = p.ld + (size_t)bh * N;
+    auto issue = [&](int jt, int buf) {
+      const uint32_t st = lds0 + buf * STAGE;
+      bwd::dma_tile<D>(Qg, N, jt * 32, st, wave, goff);
+      bwd::dma_tile<D>(dOg, N, jt * 32, st + TILE, wave, goff);
+      if (wave == 0) {
+        // lanes 0-15 bring the tile's 32 (L2, D) pairs, the rest read zeros or
+        // the next tile's pairs into the unused part of the 1 KB slot
+        const int q = jt * 32;
+        const uint32_t bytes = q < N ? (uint32_t)(N - q) * 8u : 0u;
+        lds_dma16(LDg + (q < N ? q : N), bytes, st + 2 * TILE, (uint32_t)lane * 16u);
+      }
+    };
+    if (j_first < T) issue(j_first, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int j = j_first; j < T; ++j) {
+      const int buf = (j - j_first) & 1;
+      if (j + 1 < T) issue(j + 1, buf ^ 1);
+      const int qbase = j * 32;
+      const bool wave_active = !CAUSAL || qbase + 31 >= k0w;
+      if (wave_active) {
+        const unsigned char* st = smem + buf * STAGE;
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s[r] = 0.0f;
+          dp[r] = 0.0f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < QK; ++kk) {
+          Op a, b;
+          bwd::read_rm<D>(st, rb, kk, a);
+          mfma<kBF16>(a, kop[kk], s);
+          bwd::read_rm<D>(st + TILE, rb, kk, b);
+          mfma<kBF16>(b, vop[kk], dp);
+        }
+        // (L2, D) of the lane's 16 queries qbase + 8 (r / 4) + 4 hh + r % 4
+        float l2[16], dd[16];
+        const float* ldt = (const float*)(st + 2 * TILE);
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int q4 = 8 * b4 + 4 * hh;
+          const float4 x0 = *(const float4*)(ldt + 2 * q4);
+          const float4 x1 = *(const float4*)(ldt + 2 * q4 + 4);
+          l2[4 * b4 + 0] = x0.x; dd[4 * b4 + 0] = x0.y;
+          l2[4 * b4 + 1] = x0.z; dd[4 * b4 + 1] = x0.w;
+          l2[4 * b4 + 2] = x1.x; dd[4 * b4 + 2] = x1.y;
+          l2[4 * b4 + 3] = x1.z; dd[4 * b4 + 3] = x1.w;
+        }
+        // P = exp2(S c - L2), dS = P (dP - D); query qbase + 4hh + rel is
+        // valid iff it is < N and (causal) >= the lane's key
+        const bool need_mask = (qbase + 32 > N) || (CAUSAL && qbase < k0w + 31);
+        float pv[16], ds[16];
+        if (need_mask) {
+          asm volatile("" ::: "memory");
+          const int hi = N - qbase - 4 * hh;             // rel < hi
+          const int lo = CAUSAL ? my_k - qbase - 4 * hh : -(1 << 30);   // rel >= lo
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = 8 * (r >> 2) + (r & 3);
+            const float t = (rel < hi && rel >= lo) ? __builtin_fmaf(s[r], c, -l2[r]) : -__builtin_inff();
+            pv[r] = __builtin_amdgcn_exp2f(t);
+            ds[r] = pv[r] * (dp[r] - dd[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
+            ds[r] = pv[r] * (dp[r] - dd[r]);
+          }
+        }
+        Op pop[2], dsop[2];
+        bwd::pack_b(pv, pop);
+        bwd::pack_b(ds, dsop);
+        // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed)
+#pragma unroll
+        for (int n = 0; n < PV; ++n)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            Op a, b;
+            bwd::read_tr<D>(st + TILE, rb, mb, n, a);
+            mfma<kBF16>(a, pop[n], dv[mb]);
+            bwd::read_tr<D>(st, rb, mb, n, b);
+            mfma<kBF16>(b, dsop[n], dk[mb]);
+          }
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  }
+  if (my_k < N) {
+    const size_t row = (size_t)bkv * N + my_k;
+    bwd::store_rows<MB>(p.dk, row, hh, dk, p.scale);
+    bwd::store_rows<MB>(p.dv, row, hh, dv, 1.0f);
+  }
+}
+
+}  // namespace fa

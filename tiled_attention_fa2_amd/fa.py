@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.fa_merge_partials.restype = i
         L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_fwd_gqa.restype = i
+        L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+        L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, vp, sz, vp]
+        L.fa_bwd.restype = i
         _lib = L
     return _lib
 
@@ -258,3 +262,41 @@ def quantize_qkv_fp8(q, k, v):
     k8, _ = quantize_fp8(k, descale=flat[B * H:B * H + B * Hkv])
     v8, _ = quantize_fp8(v, descale=flat[B * H + B * Hkv:])
     return q8, k8, v8, (flat.view(3, B * H) if Hkv == H else flat)
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    """Device workspace bytes fa_bwd needs (8 per query row)."""
+    return int(lib().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """FlashAttention-2 backward (bf16). q, o, do: contiguous [B, Hq, N, d];
+    k, v: [B, Hkv, N, d]; lse: float32 [B, Hq, N] from fwd. Returns
+    (dq, dk, dv) in bfloat16 with the shapes of q, k, v."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward takes bfloat16 tensors")
+    for name, t in (("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16 or t.shape != q.shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor shaped like q")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous():
+            raise ValueError(f"{name} has the wrong dtype, shape or layout")
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                      _ptr(dv), B, H, Hkv, N, d, 1 if causal else 0, float(scale), DTYPE_BF16,
+                      _ptr(workspace), workspace.numel(), _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

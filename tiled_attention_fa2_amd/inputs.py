@@ -146,3 +146,10 @@ def make_partials(S: int, BH: int, N: int, d: int, seed: int = 0, p_empty: float
     lse[empty] = float("-inf")
     o[empty] = 0.0
     return o, lse
+
+
+def make_dout(B: int, H: int, N: int, d: int, seed: int = 0):
+    """Upstream gradient dO for the backward: iid N(0,1) float32 from its own
+    seeded generator, rounded to bf16."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
