@@ -85,6 +85,29 @@ def time_fwd(fa, torch, args_in, kw, steps, warmup):
     return max(region_ms, 1e-9), kern_ms, wall_ms
 
 
+def time_bwd(fa, torch, w, qd, kd, vd, steps, warmup):
+    """The backward on the workload's own inputs: fwd once for O and L, a
+    seeded dO, then `steps` timed fa_bwd calls (HIP events on the stream)."""
+    from tiled_attention_fa2_amd.inputs import make_dout
+
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, num_splits=1)
+    do = make_dout(w.B, w.H, w.N, w.d, seed=1).to(qd.device)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=qd.device)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws)
+    kw = dict(causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+    for _ in range(warmup):
+        fa.bwd(qd, kd, vd, o, lse, do, **kw)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fa.bwd(qd, kd, vd, o, lse, do, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """Time the fp64 oracle on a bounded sample of the same workload: chunks of
     128 query rows against all N keys, cycling over heads, until budget_s."""
@@ -133,6 +156,8 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--num-splits", type=int, default=None,
                     help="key chunks of the split-KV path (default: the library's choice; 1 = unsplit)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the backward pass (bf16 workloads) into a 'bwd' object")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a kernel of known "
                          "traffic, to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -226,6 +251,17 @@ def main():
                          "kernel": kernel_name(w8, splits8),
                          "kernel_ms": round(kern8, 4)},
         }
+
+    if a.bwd and w.dtype == "bf16":
+        print("[bench] timing the backward", file=sys.stderr, flush=True)
+        msb = time_bwd(fa, torch, w, qd, kd, vd, a.steps, a.warmup)
+        fb = 2.5 * flops     # five N x N x d products against the forward's two
+        out["bwd"] = {"value": round(fb / (msb * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(msb, 4),
+                      "flop_convention": "10*B*H*N^2*d (halved for causal): dV, dP, dS-to-dQ, dS-to-dK and the "
+                                         "recomputed S; the kernels execute 14*B*H*N^2*d on MFMA (S and dP again "
+                                         "in the dQ pass)",
+                      "pct_of_mfma_peak": round(100 * fb / (msb * 1e-3) / 1e12 / peak, 2),
+                      "mfma_executed_tflops": round(1.4 * fb / (msb * 1e-3) / 1e12, 2)}
 
     if a.cpu_budget > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)

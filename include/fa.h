@@ -221,6 +221,36 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* descales, int num_splits, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
 
+/*
+ * fa_bwd -- the FlashAttention-2 backward pass, bf16 ("FlashAttention-2 from
+ * PyTorch to Triton", forward-pass section and its list of what the first
+ * kernel leaves out; "Kernels and Memory in LLM Inference", section
+ * "Training detour (brief)"). From the forward's inputs, its output O and
+ * its L, and the upstream gradient dO, with P = exp(scale Q K^T - L)
+ * recomputed tile by tile and D = rowsum(dO * O):
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * For grouped-query attention a key/value head's dK, dV sum over its group's
+ * query heads.
+ *
+ *   q, o, dout  [B, Hq, N, d] bfloat16 (o: fa_fwd's output for these inputs).
+ *   k, v        [B, Hkv, N, d] bfloat16; Hq a multiple of Hkv.
+ *   lse         [B, Hq, N] float: fa_fwd's L.
+ *   dq          [B, Hq, N, d] bfloat16 output; dk, dv [B, Hkv, N, d].
+ *   d           64 or 128.   causal, scale: as in the forward.
+ *   dtype       FA_DTYPE_BF16 only (anything else: FA_ERR_DTYPE).
+ *   workspace   device memory owned by the caller, 16-byte aligned, at least
+ *               fa_bwd_workspace_bytes(B, Hq, N) bytes: per query row the pair
+ *               (L log2 e, D) in float. Calls sharing it must not overlap.
+ * Enqueues three kernels (the (L, D) pass, then dK/dV and dQ). dQ is formed in
+ * its own pass over the key tiles, without atomics: the result is
+ * deterministic. All tensor pointers 16-byte aligned.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
 /* Human-readable name of a fa_status_t value. Never NULL. */
 const char* fa_status_string(int status);
 

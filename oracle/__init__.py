@@ -6,6 +6,6 @@ product path. It shares no code with the HIP library."""
 from .attention import attention, attention_online, attention_bruteforce  # noqa: F401
 from .splitkv import attention_keyrange, merge_partials  # noqa: F401
 from .gqa import attention_gqa, kv_head_of  # noqa: F401
-from .backward import attention_backward  # noqa: F401
+from .backward import attention_backward, attention_backward_rows  # noqa: F401
 from .fp8 import (e4m3_table, e4m3_encode, e4m3_decode, quantize_per_head,  # noqa: F401
                   dequantize_per_head, E4M3_MAX)

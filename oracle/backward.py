@@ -61,3 +61,48 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False, o=None):
             dK[b, h] = scale * (dS.T @ q[b, h])
             D[b, h] = Dr
     return dQ, dK, dV, D
+
+
+def attention_backward_rows(q, k, v, do, scale: float, causal: bool, o, q_rows, k_rows,
+                            heads=None, chunk: int = 1024):
+    """The gradients of attention_backward() evaluated only where asked: dQ at
+    the query rows q_rows and dK, dV at the key rows k_rows, for the (batch,
+    head) pairs in `heads` (default: all), for shapes whose full score matrix
+    does not fit in memory. q, k, v, do, o: [B, H, N, d] (K/V with as many
+    heads as Q). Every query row's logsumexp L comes from attention() over
+    `chunk` rows at a time; then P_ij = exp(S_ij - L_i), D_i = dO_i . O_i and
+    the same formulas as attention_backward().
+    Returns (dQ [P, Rq, d], dK [P, Rk, d], dV [P, Rk, d]) for the P pairs."""
+    from .attention import attention
+
+    B, H, N, d = q.shape
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    dQ = np.zeros((len(pairs), len(q_rows), d))
+    dK = np.zeros((len(pairs), len(k_rows), d))
+    dV = np.zeros((len(pairs), len(k_rows), d))
+    keys = np.arange(N)
+    for t, (b, h) in enumerate(pairs):
+        # one (batch, head) at a time, upcast exactly to float64
+        qh, kh, vh, doh, oh = (_as_f64(x[b:b + 1, h:h + 1])[0, 0] for x in (q, k, v, do, o))
+        L = np.concatenate([attention(qh[None, None], kh[None, None], vh[None, None], scale,
+                                      causal=causal, rows=np.arange(r0, min(N, r0 + chunk)))[1][0, 0]
+                            for r0 in range(0, N, chunk)])
+        D = np.sum(doh * oh, axis=1)
+        # query rows: dQ_i = scale sum_j P_ij (dP_ij - D_i) k_j
+        S = scale * (qh[q_rows] @ kh.T)
+        if causal:
+            S = np.where(keys[None, :] <= q_rows[:, None], S, -np.inf)
+        P = np.exp(S - L[q_rows, None])
+        dP = doh[q_rows] @ vh.T
+        dQ[t] = scale * ((P * (dP - D[q_rows, None])) @ kh)
+        # key rows: dV_j = sum_i P_ij dO_i, dK_j = scale sum_i P_ij (dP_ij - D_i) q_i
+        St = scale * (kh[k_rows] @ qh.T)          # [Rk, N] = S^T at the key rows
+        if causal:
+            St = np.where(keys[None, :] >= k_rows[:, None], St, -np.inf)
+        Pt = np.exp(St - L[None, :])
+        dPt = vh[k_rows] @ doh.T
+        dV[t] = Pt @ doh
+        dK[t] = scale * ((Pt * (dPt - D[None, :])) @ qh)
+    return dQ, dK, dV

@@ -36,7 +36,8 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_gqa", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa", "fa_fwd_splitkv",
+                                     "fa_merge_partials", "fa_quantize_fp8",
                                      "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
                                      "fa_splitkv_workspace_bytes", "fa_status_string"]
 
@@ -195,3 +196,28 @@ def _gqa(lib, Hq=8, Hkv=2, num_splits=1, ws=None, ws_bytes=0, **kw):
 ])
 def test_gqa_validation_codes(lib, kw, code):
     assert _gqa(lib, **kw) == code
+
+
+def _bwd(lib, Hq=2, Hkv=2, ws=WS, ws_bytes=1 << 40, **kw):
+    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A2, dq=A2, dk=A2, dv=A2, B=1, N=128, d=128, causal=0,
+             scale=0.1, dtype=1)
+    p.update(kw)
+    return lib.fa_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"], p["dv"],
+                      p["B"], Hq, Hkv, p["N"], p["d"], p["causal"], p["scale"], p["dtype"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(Hq=4, Hkv=3), -2), (dict(Hkv=0), -2),
+    (dict(dtype=0), -3), (dict(dtype=2), -3), (dict(d=96), -4), (dict(scale=float("nan")), -5),
+    (dict(o=None), -1), (dict(do=None), -1), (dict(lse=None), -1), (dict(dk=None), -1),
+    (dict(dq=MIS), -7), (dict(do=MIS), -7),
+    (dict(ws=None), -9), (dict(ws=ctypes.c_void_p(0x40004)), -9), (dict(ws_bytes=8 * 2 * 128 - 1), -9),
+    (dict(N=0), 0), (dict(B=0), 0),
+])
+def test_bwd_validation_codes(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def test_bwd_workspace_bytes(lib):
+    assert fa.bwd_workspace_bytes(2, 3, 100) == 8 * 2 * 3 * 100
+    assert fa.bwd_workspace_bytes(-1, 3, 100) == 0

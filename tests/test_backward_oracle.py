@@ -154,3 +154,19 @@ def test_pins_accept_the_oracle():
                                   "causal_ignored"])
 def test_pins_reject_planted_mistake(kind):
     assert not _pins_pass(_mutant(kind))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_agree_with_the_full_backward(causal):
+    q, k, v, do = _rand(2, 3, 70, 8, seed=12)
+    O, _ = oracle.attention(q, k, v, 0.35, causal=causal)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, 0.35, causal=causal, o=O)
+    q_rows = np.array([0, 1, 33, 69])
+    k_rows = np.array([0, 5, 40, 69])
+    heads = [(0, 0), (1, 2)]
+    sq, sk, sv = oracle.attention_backward_rows(q, k, v, do, 0.35, causal, O, q_rows, k_rows,
+                                                heads=heads, chunk=16)
+    for t, (b, h) in enumerate(heads):
+        assert np.allclose(sq[t], dq[b, h, q_rows], atol=1e-12)
+        assert np.allclose(sk[t], dk[b, h, k_rows], atol=1e-12)
+        assert np.allclose(sv[t], dv[b, h, k_rows], atol=1e-12)

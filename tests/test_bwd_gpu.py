@@ -111,3 +111,30 @@ def test_backward_rejects_bad_arguments():
     with pytest.raises(fa.FAError) as e:
         fa.bwd(q, k, v, o, lse, do, workspace=small)
     assert e.value.status == -9
+
+
+def test_backward_full_size_sampled():
+    # the 56-head x 30272-token DiT shape: the whole backward on the GPU,
+    # heads 0 and 55 checked on sampled query rows (dQ) and key rows (dK, dV)
+    from tiled_attention_fa2_amd.inputs import WORKLOADS, sample_rows
+    w = WORKLOADS["bf16_dit_b1_h56_n30272_d128"]
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, "bf16", seed=0)
+    do = make_dout(w.B, w.H, w.N, w.d, seed=1)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    print(f"[case] full-size backward {w.name}", flush=True)
+    o, lse = fa.fwd(qd, kd, vd, scale=w.scale, num_splits=1)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, scale=w.scale)
+    torch.cuda.synchronize()
+    q_rows = sample_rows(w.N, tile=128, n_random=16)
+    k_rows = sample_rows(w.N, tile=128, n_random=16, seed=54321)
+    heads = [(0, 0), (0, 55)]
+    rq, rk, rv = oracle.attention_backward_rows(q, k, v, do, w.scale, False, o.cpu(), q_rows, k_rows,
+                                                heads=heads)
+    for t, (b, h) in enumerate(heads):
+        for name, got, ref in (("dq", dq[b, h, q_rows], rq[t]), ("dk", dk[b, h, k_rows], rk[t]),
+                               ("dv", dv[b, h, k_rows], rv[t])):
+            g = got.float().cpu().double().numpy()
+            err = float(np.max(np.abs(g - ref)))
+            tol = 1e-2 * float(np.max(np.abs(ref))) + _floor(ref)
+            print(f"    head {h} {name}: max|err|={err:.3e} tol={tol:.3e} cos={_cos(g, ref):.7f}", flush=True)
+            assert err <= tol and _cos(g, ref) >= 0.9999, (h, name)
