@@ -30,10 +30,18 @@ KERNEL_SOURCES = ["tiled_attention_fa2_amd/csrc/fa_fwd_kernel.hpp",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the forward kernel's code: the sources with comments and blank
+    space removed, so that a change of wording alone keeps the recorded
+    traffic counters valid."""
+    import re
+
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            txt = f.read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(" ".join(txt.split()).encode())
     return h.hexdigest()
 
 

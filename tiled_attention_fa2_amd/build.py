@@ -29,6 +29,8 @@ PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
 CEILING_SRC = os.path.join(ROOT, "tests", "hip", "mfma_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_ceiling.so")
+VALU_SRC = os.path.join(ROOT, "tests", "hip", "valu_rates.hip")
+VALU_LIB = os.path.join(ROOT, "tests", "hip", "libvalu_rates.so")
 
 
 def _hipcc(cmd, verbose):
@@ -41,13 +43,15 @@ def _hipcc(cmd, verbose):
 
 
 def build_probe(verbose: bool = False) -> str:
-    """The test helpers of tests/hip: the one-wave MFMA layout/precision probe
-    and the sustained-MFMA-rate probe used by the GPU tests."""
+    """The test helpers of tests/hip: the one-wave MFMA layout/precision probe,
+    the sustained-MFMA-rate probe and the VALU issue-cost probe used by the GPU
+    tests."""
     _hipcc([HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_LIB + ".tmp"], verbose)
     os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
-    if os.path.exists(CEILING_SRC):
-        _hipcc([HIPCC, *FLAGS, CEILING_SRC, "-o", CEILING_LIB + ".tmp"], verbose)
-        os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
+    for src, lib in ((CEILING_SRC, CEILING_LIB), (VALU_SRC, VALU_LIB)):
+        if os.path.exists(src):
+            _hipcc([HIPCC, *FLAGS, src, "-o", lib + ".tmp"], verbose)
+            os.replace(lib + ".tmp", lib)
     return PROBE_LIB
 
 
