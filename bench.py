@@ -178,7 +178,7 @@ def main():
     import torch
 
     from tiled_attention_fa2_amd import fa
-    from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv, make_workload
+    from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv, make_signs, make_workload
 
     w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
@@ -246,12 +246,24 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         qms = e0.elapsed_time(e1) / a.steps
+        # the same with Q and K rotated by a randomised Hadamard transform first
+        signs = make_signs(w8.d, seed=0).to(dev)
+        fa.quantize_qkv_fp8(qd, kd, vd, signs=signs)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(a.steps):
+            fa.quantize_qkv_fp8(qd, kd, vd, signs=signs)
+        e1.record()
+        torch.cuda.synchronize()
+        rqms = e0.elapsed_time(e1) / a.steps
         v8 = w8.flops() / (ms8 * 1e-3) / 1e12
         out["fp8"] = {
             "workload": w8.name, "value": round(v8, 2), "unit": "TFLOP/s", "ms_per_step": round(ms8, 4),
             "pct_of_mfma_peak": round(100 * v8 / PEAK_TFLOPS["fp8"], 2),
             "quantize_qkv_ms": round(qms, 4),
             "value_incl_quantize": round(w8.flops() / ((ms8 + qms) * 1e-3) / 1e12, 2),
+            "quantize_qkv_rotated_ms": round(rqms, 4),
+            "value_incl_rotated_quantize": round(w8.flops() / ((ms8 + rqms) * 1e-3) / 1e12, 2),
             "roofline": {"bound": "mfma", "achieved": round(w8.flops() / (kern8 * 1e-3) / 1e12, 2),
                          "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                          "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),

@@ -111,6 +111,35 @@ int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* descale,
                     int B, int H, int N, int d, hipStream_t stream);
 
 /*
+ * fa_quantize_fp8_rotated -- randomised Hadamard rotation, then per-head FP8
+ * quantisation ("Kernels and Memory in LLM Inference", section "Precision:
+ * FP8 with a real failure mode": a fixed random rotation of Q and K before
+ * quantising spreads the few large outlier coordinates over all dimensions,
+ * and the rotations cancel in Q K^T).
+ *
+ *   x        [B, H, N, d] contiguous bfloat16 (in_dtype FA_DTYPE_BF16 only;
+ *            anything else returns FA_ERR_DTYPE), d = 64 or 128.
+ *   signs    [d] device int8: a negative entry flips that coordinate, any
+ *            other value keeps it. Q and K must be rotated with the same signs.
+ *   x_fp8    [B, H, N, d] contiguous output codes (e4m3fn) of y = (x * s) H,
+ *            H the unnormalised d x d Sylvester Hadamard matrix
+ *            (H_ij = (-1)^popcount(i & j), H H^T = d I). y is computed in
+ *            float64 (exact for bf16 rows spanning at most 38 binary orders
+ *            of magnitude) and rounded once to fp32, then quantised per head
+ *            exactly as fa_quantize_fp8 does.
+ *   descale  [B*H] device float output: amax(y) / 448 per (batch, head), 1 for
+ *            an all-zero head, times 1/d when fold_inverse_d is non-zero.
+ *            Rotate Q with fold_inverse_d = 1 and K with 0: the FP8 forward
+ *            then computes the same attention, since (Q s H)(K s H)^T = d Q K^T.
+ *   Both pointers of x and x_fp8 must be 16-byte aligned (FA_ERR_ALIGN). The
+ *   descale array is the amax accumulator while the call runs, as for
+ *   fa_quantize_fp8. Errors are returned before anything is enqueued.
+ */
+int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed char* signs, void* x_fp8,
+                            float* descale, int B, int H, int N, int d, int fold_inverse_d,
+                            hipStream_t stream);
+
+/*
  * Split-KV forward ("Kernels and Memory in LLM Inference", section
  * "Flash-Decoding: one token, whole chip": cut the keys into contiguous
  * chunks, give every chunk its own workgroup with its own running max and sum,

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa", "fa_fwd_splitkv",
-                                     "fa_merge_partials", "fa_quantize_fp8",
+                                     "fa_merge_partials", "fa_quantize_fp8", "fa_quantize_fp8_rotated",
                                      "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
                                      "fa_splitkv_workspace_bytes", "fa_status_string"]
 
@@ -104,6 +104,26 @@ def test_fwd_validation_codes(lib, kw, code):
 ])
 def test_quantize_validation_codes(lib, args, code):
     assert lib.fa_quantize_fp8(*args, None) == code
+
+
+# (x, in_dtype, signs, x_fp8, descale, B, H, N, d, fold)
+@pytest.mark.parametrize("args,code", [
+    ((A, 1, A, A2, A2, -1, 1, 16, 64, 1), -2),
+    ((A, 0, A, A2, A2, 1, 1, 16, 64, 1), -3),       # float32 input is not taken
+    ((A, 2, A, A2, A2, 1, 1, 16, 64, 1), -3),
+    ((A, 1, A, A2, A2, 1, 1, 16, 32, 0), -4),
+    ((A, 1, A, A2, A2, 1, 1, 16, 96, 0), -4),
+    ((A, 1, None, A2, A2, 1, 1, 16, 64, 0), -1),
+    ((A, 1, A, A2, None, 1, 1, 16, 64, 0), -1),
+    ((None, 1, A, A2, A2, 1, 1, 16, 64, 0), -1),
+    ((A, 1, A, None, A2, 1, 1, 16, 64, 0), -1),
+    ((MIS, 1, A, A2, A2, 1, 1, 16, 64, 0), -7),
+    ((A, 1, A, MIS, A2, 1, 1, 16, 64, 0), -7),
+    ((A, 1, A, A2, A2, 0, 4, 16, 64, 1), 0),
+    ((A, 1, A, A2, A2, 1, 1 << 17, 16, 64, 1), -2),
+])
+def test_quantize_rotated_validation_codes(lib, args, code):
+    assert lib.fa_quantize_fp8_rotated(*args, None) == code
 
 
 def test_binding_raises_when_library_missing(monkeypatch, tmp_path):

@@ -324,6 +324,46 @@ extern "C" int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* 
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed char* signs,
+                                       void* x_fp8, float* descale, int B, int H, int N, int d,
+                                       int fold_inverse_d, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  const long long BH = (long long)B * H;
+  if (BH == 0) return FA_OK;
+  if (!descale || !signs) return FA_ERR_NULL;
+  if (BH > 65535) return FA_ERR_SHAPE;  // grid.y limit of the per-head kernels
+  if (N > 0 && (!x || !x_fp8)) return FA_ERR_NULL;
+  if (N > 0 && (!aligned16(x) || !aligned16(x_fp8))) return FA_ERR_ALIGN;
+  uint32_t* amax = reinterpret_cast<uint32_t*>(descale);
+  const int nbh = (int)BH;
+
+  hipLaunchKernelGGL(fa::fa_amax_clear, dim3((nbh + 255) / 256), dim3(256), 0, stream, amax, nbh);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  if (N > 0) {
+    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
+    const int rows_per_block = 256 / (d / 8);
+    long long bph = ((long long)N + rows_per_block * 4 - 1) / (rows_per_block * 4);
+    if (bph > 256) bph = 256;
+    const dim3 grid((unsigned)bph, (unsigned)nbh);
+    if (d == 128) {
+      hipLaunchKernelGGL(fa::fa_rot_amax_kernel<128>, grid, dim3(256), 0, stream, x, signs, amax, N);
+      hipLaunchKernelGGL(fa::fa_rot_quant_kernel<128>, grid, dim3(256), 0, stream, x, signs,
+                         (uint8_t*)x_fp8, (const uint32_t*)amax, N);
+    } else {
+      hipLaunchKernelGGL(fa::fa_rot_amax_kernel<64>, grid, dim3(256), 0, stream, x, signs, amax, N);
+      hipLaunchKernelGGL(fa::fa_rot_quant_kernel<64>, grid, dim3(256), 0, stream, x, signs,
+                         (uint8_t*)x_fp8, (const uint32_t*)amax, N);
+    }
+    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  }
+  const float post = fold_inverse_d ? 1.0f / (float)d : 1.0f;
+  hipLaunchKernelGGL(fa::fa_descale_finalize_scaled, dim3((nbh + 255) / 256), dim3(256), 0, stream,
+                     amax, nbh, post);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 0 || N < 0) return 0;
   return (size_t)8 * (size_t)B * (size_t)H * (size_t)N;

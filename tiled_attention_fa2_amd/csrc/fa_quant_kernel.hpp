@@ -111,6 +111,120 @@ __global__ void __launch_bounds__(256) fa_quant_kernel(const void* x, uint8_t* o
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rotation before quantisation ("Kernels and Memory in LLM Inference", section
+// "Precision: FP8 with a real failure mode": Q and K are multiplied by a fixed
+// random rotation before FP8 quantisation, which spreads outlier coordinates;
+// the rotations cancel in Q K^T). Here the rotation is the randomised Hadamard
+// transform y = (x * s) H (s: d signs, H: the unnormalised Sylvester matrix,
+// H H^T = d I), computed as a fast Walsh-Hadamard transform in float64: every
+// partial sum of at most d signed bf16 values is exact there (unless a row
+// spans more than 38 binary orders of magnitude), so y is the exact sum
+// rounded once to fp32 whatever the order. Each row of D bf16 is handled by
+// D/8 consecutive lanes holding 8 consecutive elements each: butterflies of
+// stride 1, 2, 4 inside a lane, 8..D/2 across lanes.
+template <int D>
+__device__ __forceinline__ void rotate_row8(const void* x, size_t e0, const signed char* signs, int c,
+                                            float* y) {
+  const qu32x4 w = *(const qu32x4*)((const unsigned short*)x + e0);
+  double v[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = (double)q_u2f(w[k] << 16);
+    v[2 * k + 1] = (double)q_u2f(w[k] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    if (signs[8 * c + t] < 0) v[t] = -v[t];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if ((t & h) == 0) {
+        const double a = v[t], b = v[t + h];
+        v[t] = a + b;
+        v[t + h] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < D / 8; m <<= 1) {
+    const bool upper = (c & m) != 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const double other = __shfl_xor(v[t], m);
+      v[t] = upper ? other - v[t] : v[t] + other;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) y[t] = (float)v[t];
+}
+
+// grid = (blocks per head, B*H); rows of D bf16, D/8 lanes per row
+template <int D>
+__global__ void __launch_bounds__(256) fa_rot_amax_kernel(const void* x, const signed char* signs,
+                                                          uint32_t* amax_bits, int N) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int bh = blockIdx.y;
+  const int c = threadIdx.x % TPR;
+  float m = 0.0f;
+  // every lane runs the same trip count so that the row's shuffles stay whole
+  for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
+    const int r = r0 + threadIdx.x / TPR;
+    const int rr = r < N ? r : N - 1;          // a row past the end repeats the last one
+    float y[8];
+    rotate_row8<D>(x, ((size_t)bh * N + rr) * D + 8 * c, signs, c, y);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(y[t]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(amax_bits + bh, q_f2u(b));
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) fa_rot_quant_kernel(const void* x, const signed char* signs,
+                                                           uint8_t* out, const uint32_t* amax_bits, int N) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int bh = blockIdx.y;
+  const int c = threadIdx.x % TPR;
+  const float amax = q_u2f(amax_bits[bh]);
+  const float mult = amax == 0.0f ? 1.0f : 448.0f / amax;
+  for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
+    const int r = r0 + threadIdx.x / TPR;
+    const int rr = r < N ? r : N - 1;
+    float y[8];
+    rotate_row8<D>(x, ((size_t)bh * N + rr) * D + 8 * c, signs, c, y);
+    uint2 o;
+    int pk0 = 0, pk1 = 0;
+    float z[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) z[t] = fminf(fmaxf(y[t] * mult, -448.0f), 448.0f);
+    pk0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], pk0, false);
+    pk0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pk0, true);
+    pk1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[4], z[5], pk1, false);
+    pk1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[6], z[7], pk1, true);
+    o.x = (uint32_t)pk0;
+    o.y = (uint32_t)pk1;
+    if (r < N) *(uint2*)(out + ((size_t)bh * N + r) * D + 8 * c) = o;
+  }
+}
+
+// amax (bit pattern, in place) -> descale = amax / 448 (or 1 for amax == 0),
+// times `post` (1, or the exact power of two 1/d for a rotated Q)
+__global__ void fa_descale_finalize_scaled(uint32_t* amax_bits_then_descale, int n, float post) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float amax = q_u2f(amax_bits_then_descale[i]);
+    const float ds = amax == 0.0f ? 1.0f : amax / 448.0f;
+    amax_bits_then_descale[i] = q_f2u(ds * post);
+  }
+}
+
 // amax (bit pattern, in place) -> descale = amax / 448, or 1 for amax == 0
 __global__ void fa_descale_finalize(uint32_t* amax_bits_then_descale, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;

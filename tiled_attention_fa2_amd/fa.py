@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_quantize_fp8.argtypes = [vp, i, vp, vp, i, i, i, i, vp]
         L.fa_quantize_fp8.restype = i
+        L.fa_quantize_fp8_rotated.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, vp]
+        L.fa_quantize_fp8_rotated.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         sz = ctypes.c_size_t
@@ -251,15 +253,48 @@ def quantize_fp8(x, out=None, descale=None):
     return out, descale
 
 
-def quantize_qkv_fp8(q, k, v):
+def quantize_fp8_rotated(x, signs, fold_inverse_d: bool, out=None, descale=None):
+    """Randomised Hadamard rotation y = (x * signs) H of a contiguous
+    [B, H, N, d] bfloat16 device tensor, then per-head e4m3 quantisation of y.
+    signs: int8 [d] device tensor of +1 / -1. With fold_inverse_d the descale
+    also carries 1/d (for Q). Returns (codes uint8 [B, H, N, d],
+    descale float32 [B*H])."""
+    if not x.is_cuda or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] device tensor")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("quantize_fp8_rotated takes bfloat16")
+    B, H, N, d = x.shape
+    if (not signs.is_cuda or signs.dtype != torch.int8 or signs.dim() != 1
+            or signs.numel() != d or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous int8 [d] device tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
+    st = lib().fa_quantize_fp8_rotated(_ptr(x), DTYPE_BF16, _ptr(signs), _ptr(out), _ptr(descale),
+                                       B, H, N, d, 1 if fold_inverse_d else 0, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_fp8_rotated")
+    return out, descale
+
+
+def quantize_qkv_fp8(q, k, v, signs=None):
     """Quantise Q, K and V per head. Returns (q8, k8, v8, descales): descales
     [3, B*H] when Q, K and V have the same heads, else the flat
-    B*Hq + 2*B*Hkv layout fwd() takes for grouped-query attention."""
+    B*Hq + 2*B*Hkv layout fwd() takes for grouped-query attention.
+    With signs (int8 [d] device tensor of +1 / -1), Q and K are rotated by
+    the randomised Hadamard transform before quantising, 1/d folded into Q's
+    descales; V is quantised as it is. fwd() on the result computes the same
+    attention (the rotations cancel in Q K^T)."""
     B, H = q.shape[:2]
     Hkv = k.shape[1]
     flat = torch.empty(B * H + 2 * B * Hkv, dtype=torch.float32, device=q.device)
-    q8, _ = quantize_fp8(q, descale=flat[:B * H])
-    k8, _ = quantize_fp8(k, descale=flat[B * H:B * H + B * Hkv])
+    if signs is None:
+        q8, _ = quantize_fp8(q, descale=flat[:B * H])
+        k8, _ = quantize_fp8(k, descale=flat[B * H:B * H + B * Hkv])
+    else:
+        q8, _ = quantize_fp8_rotated(q, signs, True, descale=flat[:B * H])
+        k8, _ = quantize_fp8_rotated(k, signs, False, descale=flat[B * H:B * H + B * Hkv])
     v8, _ = quantize_fp8(v, descale=flat[B * H + B * Hkv:])
     return q8, k8, v8, (flat.view(3, B * H) if Hkv == H else flat)
 

@@ -153,3 +153,11 @@ def make_dout(B: int, H: int, N: int, d: int, seed: int = 0):
     seeded generator, rounded to bf16."""
     g = torch.Generator().manual_seed(seed)
     return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_signs(d: int, seed: int = 0):
+    """The d random signs of a randomised Hadamard rotation, drawn from their
+    own seeded generator: int8 [d] of +1 / -1, each with probability 1/2."""
+    g = torch.Generator().manual_seed(seed)
+    bits = torch.randint(0, 2, (d,), generator=g, dtype=torch.int64)
+    return (1 - 2 * bits).to(torch.int8)
