@@ -65,18 +65,20 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def time_fwd(fa, torch, args_in, kw, steps, warmup):
-    """Warm up, then time exactly `steps` launches. Returns (region ms per
-    step, mean kernel ms from per-launch events)."""
+def time_fwd(fa, torch, args_in, kw, steps, warmup, fn=None):
+    """Warm up, then time exactly `steps` launches of fn (default fa.fwd).
+    Returns (region ms per step, mean kernel ms from per-launch events, wall
+    ms per step)."""
+    fn = fa.fwd if fn is None else fn
     splits = kw.get("num_splits") or 1
     if splits > 1:   # the split-KV workspace, allocated once outside the timed region
         B, H, N, d = args_in[0].shape
         kw = dict(kw, workspace=torch.empty(fa.splitkv_workspace_bytes(B, H, N, d, splits),
                                             dtype=torch.uint8, device=args_in[0].device))
-    o, lse = fa.fwd(*args_in, **kw)
+    o, lse = fn(*args_in, **kw)
     kw = dict(kw, out=o, lse=lse)
     for _ in range(warmup):
-        fa.fwd(*args_in, **kw)
+        fn(*args_in, **kw)
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -84,7 +86,7 @@ def time_fwd(fa, torch, args_in, kw, steps, warmup):
     t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record(stream)
-        fa.fwd(*args_in, **kw)
+        fn(*args_in, **kw)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
@@ -256,6 +258,20 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         rqms = e0.elapsed_time(e1) / a.steps
+        # per-block FP8: row-block quantise of Q and K, key-block quantise of
+        # V (one pass each), then the forward with the scales in the MFMAs
+        mq8, mk8, mv8, msc = fa.quantize_qkv_mxfp8(qd, kd, vd)
+        msm, mskern, _ = time_fwd(fa, torch, (mq8, mk8, mv8, msc),
+                                  dict(causal=False, scale=w8.scale, num_splits=splits8),
+                                  a.steps, a.warmup, fn=fa.fwd_mxfp8)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(a.steps):
+            fa.quantize_qkv_mxfp8(qd, kd, vd)
+        e1.record()
+        torch.cuda.synchronize()
+        mqms = e0.elapsed_time(e1) / a.steps
+        del mq8, mk8, mv8, msc
         v8 = w8.flops() / (ms8 * 1e-3) / 1e12
         out["fp8"] = {
             "workload": w8.name, "value": round(v8, 2), "unit": "TFLOP/s", "ms_per_step": round(ms8, 4),
@@ -264,6 +280,12 @@ def main():
             "value_incl_quantize": round(w8.flops() / ((ms8 + qms) * 1e-3) / 1e12, 2),
             "quantize_qkv_rotated_ms": round(rqms, 4),
             "value_incl_rotated_quantize": round(w8.flops() / ((ms8 + rqms) * 1e-3) / 1e12, 2),
+            "per_block": {"value": round(w8.flops() / (msm * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                          "ms_per_step": round(msm, 4), "kernel_ms": round(mskern, 4),
+                          "pct_of_mfma_peak": round(100 * w8.flops() / (msm * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 2),
+                          "quantize_qkv_ms": round(mqms, 4),
+                          "value_incl_quantize": round(w8.flops() / ((msm + mqms) * 1e-3) / 1e12, 2),
+                          "scales": "E8M0 per 32 elements along each product's contraction axis"},
             "roofline": {"bound": "mfma", "achieved": round(w8.flops() / (kern8 * 1e-3) / 1e12, 2),
                          "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                          "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),

@@ -140,6 +140,71 @@ int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed char* sign
                             hipStream_t stream);
 
 /*
+ * Per-block FP8 ("Kernels and Memory in LLM Inference", section "Precision:
+ * FP8 with a real failure mode": one scale per block of values, so that an
+ * outlier widens only its own block's grid instead of the whole tensor's).
+ *
+ * A block is 32 consecutive elements along the axis the product it feeds
+ * sums over, as in the OCP microscaling (MX) formats: 32 elements of one row
+ * for Q and K (S = Q K^T sums over d), 32 keys of one column for V (O = P V
+ * sums over the keys; the last block of a head holds the N mod 32 keys that
+ * remain). Each block has a power-of-two scale 2^e stored as the E8M0 byte
+ * e + 127, where e is the smallest integer with amax(block) <= 448 * 2^e
+ * (nothing saturates), clamped to [-127, 127] (an all-zero block gets 0x00);
+ * the codes are e4m3fn round-to-nearest-even of x * 2^-e, and the value of a
+ * code is its e4m3 value times 2^e. Non-finite inputs give unspecified codes.
+ */
+
+/*
+ * fa_quantize_mxfp8_rows -- row blocks (for Q and K).
+ *   x        [B, H, N, d] contiguous float (FA_DTYPE_F32) or bfloat16
+ *            (FA_DTYPE_BF16), d = 64 or 128, 16-byte aligned.
+ *   signs    NULL, or [d] device int8: the input rows are first rotated by
+ *            the randomised Hadamard transform of fa_quantize_fp8_rotated
+ *            (exact float64 sums rounded once to fp32; bfloat16 input only,
+ *            else FA_ERR_DTYPE).
+ *   fold_inverse_d  non-zero: the (rotated) values are multiplied by the
+ *            power of two 1/d in fp32 before quantising (for a rotated Q).
+ *   x_fp8    [B, H, N, d] contiguous e4m3fn codes, 16-byte aligned.
+ *   scales   [B, H, N, d/32] E8M0 bytes.
+ * One pass; every block is independent. Returns before launching on errors.
+ */
+int fa_quantize_mxfp8_rows(const void* x, int in_dtype, const signed char* signs, int fold_inverse_d,
+                           void* x_fp8, unsigned char* scales, int B, int H, int N, int d,
+                           hipStream_t stream);
+
+/*
+ * fa_quantize_mxfp8_keys -- key blocks (for V).
+ *   x        [B, H, N, d] contiguous float or bfloat16, 16-byte aligned.
+ *   x_fp8    [B, H, N, d] contiguous e4m3fn codes, 16-byte aligned.
+ *   scales   [B, H, ceil(N/32), d] E8M0 bytes, 4-byte aligned: the scale of
+ *            keys 32c .. 32c + 31 of column j at [b][h][c][j].
+ */
+int fa_quantize_mxfp8_keys(const void* x, int in_dtype, void* x_fp8, unsigned char* scales,
+                           int B, int H, int N, int d, hipStream_t stream);
+
+/*
+ * fa_fwd_mxfp8 -- the FP8 forward on per-block codes. The block scales are
+ * applied inside gfx950's scaled matrix instructions (no extra arithmetic per
+ * score); the softmax, P's FP8 rounding and the outputs are those of fa_fwd
+ * with dtype FA_DTYPE_FP8_E4M3, with the dequantised values
+ * code * 2^(scale - 127) in place of code * descale.
+ *   q         [B, Hq, N, d] codes with q_scales [B, Hq, N, d/32];
+ *   k         [B, Hkv, N, d] codes with k_scales [B, Hkv, N, d/32];
+ *   v         [B, Hkv, N, d] codes with v_scales [B, Hkv, ceil(N/32), d];
+ *             Hq a multiple of Hkv (query head h reads K/V head h / (Hq/Hkv)).
+ *   o, lse    as fa_fwd (bf16 O [B, Hq, N, d], fp32 L [B, Hq, N]).
+ *   d must be 128 (FA_ERR_HEAD_DIM otherwise). Missing scale arrays return
+ *   FA_ERR_DESCALES, scale arrays not 4-byte aligned FA_ERR_ALIGN.
+ *   num_splits 1 runs unsplit (workspace unused); 2..FA_MAX_SPLITS run the
+ *   split-KV path with the workspace of fa_fwd_splitkv.
+ */
+int fa_fwd_mxfp8(const void* q, const void* k, const void* v, const unsigned char* q_scales,
+                 const unsigned char* k_scales, const unsigned char* v_scales, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale, int num_splits,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Split-KV forward ("Kernels and Memory in LLM Inference", section
  * "Flash-Decoding: one token, whole chip": cut the keys into contiguous
  * chunks, give every chunk its own workgroup with its own running max and sum,

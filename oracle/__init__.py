@@ -10,4 +10,4 @@ from .backward import attention_backward, attention_backward_rows  # noqa: F401
 from .rotation import hadamard, rotate, quantize_rotated  # noqa: F401
 from .fp8 import (e4m3_table, e4m3_encode, e4m3_decode, quantize_per_head,  # noqa: F401
                   dequantize_per_head, E4M3_MAX)
-from .mxfp8 import mx_exponent, quantize_mx, dequantize_mx, quantize_qkv_mx  # noqa: F401
+from .mxfp8 import mx_exponent, quantize_mx, dequantize_mx, quantize_qkv_mx, quantize_rotated_mx  # noqa: F401

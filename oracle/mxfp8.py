@@ -114,3 +114,16 @@ def dequantize_mx(codes, scales, axis: str) -> np.ndarray:
 def quantize_qkv_mx(q, k, v):
     """Q and K by rows, V by keys. Returns ((q8, qs), (k8, ks), (v8, vs))."""
     return quantize_mx(q, "rows"), quantize_mx(k, "rows"), quantize_mx(v, "keys")
+
+
+def quantize_rotated_mx(x, signs, fold_inverse_d: bool):
+    """Row blocks of the randomised Hadamard rotation of x (rotation.rotate:
+    exact float64 sums rounded once to fp32), multiplied in fp32 by the power
+    of two 1/d when fold_inverse_d (for Q: the rotations of Q and K then
+    cancel exactly in Q K^T). Returns quantize_mx(..., "rows")'s output."""
+    from .rotation import rotate
+
+    y = rotate(x, signs)
+    if fold_inverse_d:
+        y = (y * np.float32(1.0 / y.shape[-1])).astype(np.float32)
+    return quantize_mx(y, "rows")

@@ -40,6 +40,37 @@ __global__ void probe_fp8_kernel(const int* a, const int* b, float* c) {
   for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
 }
 
+// The scaled fp8 MFMA with a 32-bit scale register per lane for each operand;
+// OPA / OPB pick the byte of that register the instruction uses (E8M0:
+// 2^(byte - 127)).
+template <int OPA, int OPB>
+__global__ void probe_fp8_scaled_kernel(const int* a, const int* b, const int* sa, const int* sb,
+                                        float* c) {
+  const int l = threadIdx.x;
+  f32x16 acc = {};
+  i32x8 av, bv;
+  for (int s = 0; s < 8; ++s) {
+    av[s] = a[l * 8 + s];
+    bv[s] = b[l * 8 + s];
+  }
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, OPA, sa[l], OPB, sb[l]);
+  for (int r = 0; r < 16; ++r) c[l * 16 + r] = acc[r];
+}
+
+// variant 0: bytes (0, 0); 1: (2, 1); 2: (3, 3). a, b: 64 x 32 codes; sa, sb:
+// 64 scale registers; c: 64 x 16 floats.
+extern "C" int probe_mfma_scaled(int variant, const void* a, const void* b, const void* sa,
+                                 const void* sb, float* c) {
+  const int *pa = (const int*)a, *pb = (const int*)b, *psa = (const int*)sa, *psb = (const int*)sb;
+  if (variant == 0)
+    hipLaunchKernelGGL((probe_fp8_scaled_kernel<0, 0>), dim3(1), dim3(64), 0, 0, pa, pb, psa, psb, c);
+  else if (variant == 1)
+    hipLaunchKernelGGL((probe_fp8_scaled_kernel<2, 1>), dim3(1), dim3(64), 0, 0, pa, pb, psa, psb, c);
+  else
+    hipLaunchKernelGGL((probe_fp8_scaled_kernel<3, 3>), dim3(1), dim3(64), 0, 0, pa, pb, psa, psb, c);
+  return (int)hipDeviceSynchronize();
+}
+
 extern "C" int probe_mfma(int kind, const void* a, const void* b, float* c) {
   if (kind == 0)
     hipLaunchKernelGGL(probe_f32_kernel, dim3(1), dim3(64), 0, 0, (const float*)a, (const float*)b, c);

@@ -36,8 +36,9 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa", "fa_fwd_splitkv",
-                                     "fa_merge_partials", "fa_quantize_fp8", "fa_quantize_fp8_rotated",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa",
+                                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8", "fa_quantize_fp8_rotated",
+                                     "fa_quantize_mxfp8_keys", "fa_quantize_mxfp8_rows",
                                      "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
                                      "fa_splitkv_workspace_bytes", "fa_status_string"]
 
@@ -124,6 +125,56 @@ def test_quantize_validation_codes(lib, args, code):
 ])
 def test_quantize_rotated_validation_codes(lib, args, code):
     assert lib.fa_quantize_fp8_rotated(*args, None) == code
+
+
+# (x, in_dtype, signs, fold, x_fp8, scales, B, H, N, d)
+@pytest.mark.parametrize("args,code", [
+    ((A, 1, None, 0, A2, A2, -1, 1, 16, 64), -2),
+    ((A, 2, None, 0, A2, A2, 1, 1, 16, 64), -3),
+    ((A, 0, A, 0, A2, A2, 1, 1, 16, 64), -3),        # rotation needs bfloat16
+    ((A, 1, None, 0, A2, A2, 1, 1, 16, 96), -4),
+    ((None, 1, None, 0, A2, A2, 1, 1, 16, 64), -1),
+    ((A, 1, None, 0, None, A2, 1, 1, 16, 64), -1),
+    ((A, 1, None, 0, A2, None, 1, 1, 16, 64), -1),
+    ((MIS, 1, None, 0, A2, A2, 1, 1, 16, 64), -7),
+    ((A, 1, None, 0, MIS, A2, 1, 1, 16, 64), -7),
+    ((A, 1, None, 0, A2, A2, 0, 4, 16, 64), 0),
+    ((A, 1, None, 0, A2, A2, 1, 1, 0, 64), 0),
+    ((A, 1, A, 1, A2, A2, 1, 1 << 17, 16, 64), -2),
+])
+def test_quantize_mxfp8_rows_validation_codes(lib, args, code):
+    assert lib.fa_quantize_mxfp8_rows(*args, None) == code
+
+
+# (x, in_dtype, x_fp8, scales, B, H, N, d)
+@pytest.mark.parametrize("args,code", [
+    ((A, 1, A2, A2, -1, 1, 16, 64), -2),
+    ((A, 7, A2, A2, 1, 1, 16, 64), -3),
+    ((A, 1, A2, A2, 1, 1, 16, 32), -4),
+    ((A, 1, None, A2, 1, 1, 16, 64), -1),
+    ((A, 1, A2, None, 1, 1, 16, 64), -1),
+    ((MIS, 1, A2, A2, 1, 1, 16, 64), -7),
+    ((A, 1, A2, ctypes.c_void_p(0x20002), 1, 1, 16, 64), -7),
+    ((A, 1, A2, A2, 1, 0, 16, 64), 0),
+])
+def test_quantize_mxfp8_keys_validation_codes(lib, args, code):
+    assert lib.fa_quantize_mxfp8_keys(*args, None) == code
+
+
+def _fwd_mx(lib, q=A, k=A, v=A, qs=A2, ks=A2, vs=A2, o=A2, lse=A2, B=1, Hq=2, Hkv=1, N=128, d=128, causal=0,
+            scale=0.1, splits=1, ws=None, wsb=0):
+    return lib.fa_fwd_mxfp8(q, k, v, qs, ks, vs, o, lse, B, Hq, Hkv, N, d, causal, scale, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(Hkv=3), -2), (dict(d=64), -4), (dict(d=96), -4),
+    (dict(scale=float("nan")), -5), (dict(qs=None), -6), (dict(vs=None), -6),
+    (dict(q=None), -1), (dict(q=MIS), -7), (dict(ks=ctypes.c_void_p(0x20001)), -7),
+    (dict(splits=0), -10), (dict(splits=65), -10), (dict(splits=2), -9),
+    (dict(N=0), 0), (dict(B=0), 0),
+])
+def test_fwd_mxfp8_validation_codes(lib, kw, code):
+    assert _fwd_mx(lib, **kw) == code
 
 
 def test_binding_raises_when_library_missing(monkeypatch, tmp_path):

@@ -148,10 +148,11 @@ def _fp8_outlier_bounds(ref_in, scale, floor):
     from test_mfma_layout_gpu import EPS_FP8_ACC
 
     qd, kd, vd = ref_in
+    group = qd.shape[1] // kd.shape[1]          # query heads per K/V head
     ds = 0.0
     for b in range(qd.shape[0]):
         for h in range(qd.shape[1]):
-            ds = max(ds, float(np.max(np.abs(qd[b, h]) @ np.abs(kd[b, h]).T)))
+            ds = max(ds, float(np.max(np.abs(qd[b, h]) @ np.abs(kd[b, h // group]).T)))
     dS = EPS_FP8_ACC * abs(scale) * ds
     vmax = float(np.max(np.abs(vd)))
     return TOL_O["fp8"] + floor + 2.0 ** -4 * vmax + 2 * dS * vmax, TOL_L + dS

@@ -95,3 +95,48 @@ def test_fp8_mfma_accumulation_precision():
     worst = max(worst, float(np.max(np.abs(got - exp) / mag)))
     print(f"fp8 MFMA: max |err| / sum|a*b| = {worst:.3e} (2^{np.log2(max(worst, 1e-30)):.1f})")
     assert worst <= EPS_FP8_ACC
+
+
+def _probe_scaled(variant, ac, bc, sa, sb):
+    lib = ctypes.CDLL(LIB)
+    lib.probe_mfma_scaled.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 5
+    dev = [torch.from_numpy(np.ascontiguousarray(x)).cuda()
+           for x in (ac.astype(np.uint8), bc.astype(np.uint8), sa.astype(np.uint32), sb.astype(np.uint32))]
+    a, b, sa_d, sb_d = (t.view(torch.int32) for t in dev)
+    c = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    assert lib.probe_mfma_scaled(variant, a.data_ptr(), b.data_ptr(), sa_d.data_ptr(), sb_d.data_ptr(),
+                                 c.data_ptr()) == 0
+    return c.cpu().numpy().reshape(64, 16)
+
+
+@pytest.mark.parametrize("variant,opa,opb", [(0, 0, 0), (1, 2, 1), (2, 3, 3)])
+def test_fp8_scaled_mfma_per_lane_scales(variant, opa, opb):
+    # The per-block FP8 path relies on this layout of the scaled fp8 MFMA
+    # (32x32x64): lane half h slot s holds k = 32 (s // 16) + 16 h + s % 16, so
+    # the contraction block b (k = 32b .. 32b + 31) is slots 16b .. 16b + 15
+    # of both lane halves, and its E8M0 scale for row i of A (column j of B)
+    # comes from lane i + 32b (j + 32b); opsel picks the byte of that lane's
+    # scale register.
+    rng = np.random.default_rng(10 + variant)
+    sg = lambda: rng.integers(0, 2, 64 * 32) * 0x80
+    ac = rng.integers(0x30, 0x40, 64 * 32) | sg()
+    bc = rng.integers(0x30, 0x40, 64 * 32) | sg()
+    # scales 2^-1 .. 2^1 keep every sum exact in fp32 (multiples of 2^-10 below 2^10)
+    sa_bytes = rng.integers(126, 129, (64, 4))
+    sb_bytes = rng.integers(126, 129, (64, 4))
+    pack = lambda by: (by[:, 0] | (by[:, 1] << 8) | (by[:, 2] << 16) | (by[:, 3] << 24)).astype(np.uint32)
+    got = _probe_scaled(variant, ac, bc, pack(sa_bytes), pack(sb_bytes))
+    tab = oracle.e4m3_table()
+    av, bv = tab[ac.reshape(64, 32)], tab[bc.reshape(64, 32)]
+    A = np.zeros((32, 64))
+    B = np.zeros((64, 32))
+    for l in range(64):
+        i, h = l % 32, l // 32
+        for sl in range(32):
+            blk = sl // 16
+            k = 32 * blk + 16 * h + sl % 16
+            A[i, k] = av[l, sl] * 2.0 ** (sa_bytes[i + 32 * blk, opa] - 127)
+            B[k, i] = bv[l, sl] * 2.0 ** (sb_bytes[i + 32 * blk, opb] - 127)
+    exp = _expected(A, B)
+    print(f"max |got - expected| = {np.max(np.abs(got - exp)):.3e}, max |expected| = {np.max(np.abs(exp)):.3e}")
+    assert np.array_equal(got, exp)

@@ -186,6 +186,24 @@ def test_attention_on_dequantised_blocks_is_close():
     assert a @ b / (np.linalg.norm(a) * np.linalg.norm(b)) > 0.999
 
 
+def test_rotated_blocks_restore_the_scores():
+    # rotated Q (1/d folded in) times rotated K^T gives back Q K^T; the fold is
+    # exactly a factor 1/d on the values (a power of two moves only exponents)
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn((1, 2, 50, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 2, 50, 128), generator=g).to(torch.bfloat16)
+    q[..., 9] *= 30.0
+    s = (1 - 2 * torch.randint(0, 2, (128,), generator=g)).numpy()
+    qd = oracle.dequantize_mx(*oracle.quantize_rotated_mx(q, s, True), "rows")
+    kd = oracle.dequantize_mx(*oracle.quantize_rotated_mx(k, s, False), "rows")
+    S = np.einsum("bhnd,bhmd->bhnm", qd, kd)
+    S_ref = np.einsum("bhnd,bhmd->bhnm", q.double().numpy(), k.double().numpy())
+    assert np.corrcoef(S.ravel(), S_ref.ravel())[0, 1] > 0.999
+    assert np.max(np.abs(S - S_ref)) < 0.1 * np.max(np.abs(S_ref))
+    q_nofold = oracle.dequantize_mx(*oracle.quantize_rotated_mx(q, s, False), "rows")
+    assert np.array_equal(qd * 128, q_nofold)
+
+
 # --------------------------------------------------------------------------
 # planted mistakes
 # --------------------------------------------------------------------------

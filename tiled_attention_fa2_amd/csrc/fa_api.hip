@@ -23,22 +23,23 @@ constexpr int kWavesPerSimd = 2;
 // transpose reads (the shapes the DiT benchmark runs). bf16: key tile 32,
 // three stages, three waves per SIMD; fp8: key tile 64, two stages, three
 // waves per SIMD.
-template <int DT, bool CAUSAL, bool SPLIT>
+// MX: per-block FP8 scales (fp8 only), same tiles as plain fp8.
+template <int DT, bool CAUSAL, bool SPLIT, bool MX = false>
 void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
   constexpr int BN = DT == fa::kBF16 ? 32 : 64;
   constexpr int NSTAGE = DT == fa::kBF16 ? 3 : 2;
   constexpr int LOOK = 2, WPE = 3;
   const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
-  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT>),
+  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX>),
                      dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
 }
 
-template <int DT>
+template <int DT, bool MX = false>
 int launch_fwd_dma(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
   if (causal)
-    split ? launch_fwd_dma_inst<DT, true, true>(a, stream) : launch_fwd_dma_inst<DT, true, false>(a, stream);
+    split ? launch_fwd_dma_inst<DT, true, true, MX>(a, stream) : launch_fwd_dma_inst<DT, true, false, MX>(a, stream);
   else
-    split ? launch_fwd_dma_inst<DT, false, true>(a, stream) : launch_fwd_dma_inst<DT, false, false>(a, stream);
+    split ? launch_fwd_dma_inst<DT, false, true, MX>(a, stream) : launch_fwd_dma_inst<DT, false, false, MX>(a, stream);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -59,9 +60,11 @@ int launch_fwd(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-// Kernel choice by dtype and head dim (validated by the caller).
-int launch_any(const fa::FwdArgs& a, int dtype, int d, bool split, hipStream_t stream) {
+// Kernel choice by dtype and head dim (validated by the caller); mx selects
+// the per-block FP8 kernel (fp8, head dim 128).
+int launch_any(const fa::FwdArgs& a, int dtype, int d, bool split, bool mx, hipStream_t stream) {
   const bool c = a.causal != 0;
+  if (mx) return launch_fwd_dma<fa::kFP8, true>(a, c, split, stream);
   switch (dtype) {
     case FA_DTYPE_BF16:
       return d == 128 ? launch_fwd_dma<fa::kBF16>(a, c, split, stream)
@@ -80,23 +83,33 @@ constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 // Argument checks shared by fa_fwd and fa_fwd_splitkv, in the documented
 // order; fills the kernel arguments. Returns FA_OK with *empty = true when
 // there is nothing to compute.
+// E8M0 block scales of the per-block FP8 forward (null for the other paths).
+struct MxScales {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+};
+
 int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
-                fa::FwdArgs& a, bool& empty);
+                const MxScales* mx, fa::FwdArgs& a, bool& empty);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
-                fa::FwdArgs& a, bool& empty) {
+                const MxScales* mx, fa::FwdArgs& a, bool& empty) {
   empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (H > 0 && (Hkv < 1 || H % Hkv != 0)) return FA_ERR_SHAPE;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
     return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (mx && d != 128) return FA_ERR_HEAD_DIM;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
-  if (dtype == FA_DTYPE_FP8_E4M3 && descales == nullptr) return FA_ERR_DESCALES;
+  if (mx && (!mx->q || !mx->k || !mx->v)) return FA_ERR_DESCALES;
+  if (!mx && dtype == FA_DTYPE_FP8_E4M3 && descales == nullptr) return FA_ERR_DESCALES;
   const long long BH = (long long)B * H;
   if (BH == 0 || N == 0) {
     empty = true;
@@ -104,6 +117,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   }
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (mx && (!aligned4(mx->q) || !aligned4(mx->k) || !aligned4(mx->v))) return FA_ERR_ALIGN;
   const long long n_qtiles = ((long long)N + kBM - 1) / kBM;
   if (BH > INT_MAX || BH * n_qtiles > INT_MAX) return FA_ERR_SHAPE;
   // one head of Q, K or V is addressed with 32-bit buffer offsets
@@ -123,6 +137,11 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.group = H / Hkv;
+  if (mx) {
+    a.q_scale = mx->q;
+    a.k_scale = mx->k;
+    a.v_scale = mx->v;
+  }
   return FA_OK;
 }
 
@@ -166,12 +185,13 @@ namespace {
 // split-KV kernels and the merge in `workspace`.
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
             int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
-            int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+            const MxScales* mx, int num_splits, void* workspace, size_t workspace_bytes,
+            hipStream_t stream) {
   fa::FwdArgs a;
   bool empty = false;
-  const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, a, empty);
+  const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, mx, a, empty);
   if (st != FA_OK) return st;
-  if (num_splits == 0) return empty ? FA_OK : launch_any(a, dtype, d, false, stream);
+  if (num_splits == 0) return empty ? FA_OK : launch_any(a, dtype, d, false, mx != nullptr, stream);
   if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
   if (empty) return FA_OK;
   const size_t need = fa_splitkv_workspace_bytes(B, Hq, N, d, num_splits);
@@ -185,7 +205,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.split_keys = chunk;
   a.o_part = o_parts;
   a.lse_part = lse_parts;
-  const int r = launch_any(a, dtype, d, true, stream);
+  const int r = launch_any(a, dtype, d, true, mx != nullptr, stream);
   if (r != FA_OK) return r;
   return fa_merge_partials(o_parts, lse_parts, used, B, Hq, N, d,
                            dtype == FA_DTYPE_F32 ? FA_DTYPE_F32 : FA_DTYPE_BF16, o, lse, stream);
@@ -196,7 +216,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int N, int d, int causal, float scale, int dtype,
                       const float* descales, hipStream_t stream) {
-  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, 0, nullptr, 0, stream);
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, 0, nullptr, 0,
+                 stream);
 }
 
 extern "C" int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -207,10 +228,27 @@ extern "C" int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, 
     // shape and argument errors come first, as for the other entry points
     fa::FwdArgs a;
     bool empty = false;
-    const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, a, empty);
+    const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, nullptr,
+                               a, empty);
     return st != FA_OK ? st : FA_ERR_SPLITS;
   }
-  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales,
+  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, descales, nullptr,
+                 num_splits == 1 ? 0 : num_splits, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa_fwd_mxfp8(const void* q, const void* k, const void* v, const unsigned char* q_scales,
+                            const unsigned char* k_scales, const unsigned char* v_scales, void* o,
+                            float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                            int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const MxScales mx{q_scales, k_scales, v_scales};
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) {
+    fa::FwdArgs a;
+    bool empty = false;
+    const int st = prepare_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, FA_DTYPE_FP8_E4M3, nullptr,
+                               &mx, a, empty);
+    return st != FA_OK ? st : FA_ERR_SPLITS;
+  }
+  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, FA_DTYPE_FP8_E4M3, nullptr, &mx,
                  num_splits == 1 ? 0 : num_splits, workspace, workspace_bytes, stream);
 }
 
@@ -281,7 +319,7 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
                               const float* descales, int num_splits, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
   if (num_splits == 0) num_splits = -1;   // 0 selects the unsplit path inside run_fwd
-  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, num_splits,
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, num_splits,
                  workspace, workspace_bytes, stream);
 }
 
@@ -361,6 +399,77 @@ extern "C" int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed
   const float post = fold_inverse_d ? 1.0f / (float)d : 1.0f;
   hipLaunchKernelGGL(fa::fa_descale_finalize_scaled, dim3((nbh + 255) / 256), dim3(256), 0, stream,
                      amax, nbh, post);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_quantize_mxfp8_rows(const void* x, int in_dtype, const signed char* signs,
+                                      int fold_inverse_d, void* x_fp8, unsigned char* scales, int B,
+                                      int H, int N, int d, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (signs && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  const long long BH = (long long)B * H;
+  if (BH == 0 || N == 0) return FA_OK;
+  if (!x || !x_fp8 || !scales) return FA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_fp8)) return FA_ERR_ALIGN;
+  const float post = fold_inverse_d ? 1.0f / (float)d : 1.0f;
+  if (!signs) {
+    const long long nblocks = BH * N * (d / 32);
+    const long long grid = ceil_div(nblocks, 256);
+    if (grid > INT_MAX) return FA_ERR_SHAPE;
+    if (in_dtype == FA_DTYPE_BF16)
+      hipLaunchKernelGGL(fa::fa_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                         (uint8_t*)x_fp8, scales, nblocks, post);
+    else
+      hipLaunchKernelGGL(fa::fa_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                         (uint8_t*)x_fp8, scales, nblocks, post);
+  } else {
+    if (BH > 65535) return FA_ERR_SHAPE;   // grid.y limit of the per-head kernel
+    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
+    const int rows_per_block = 256 / (d / 8);
+    long long bph = ceil_div(N, rows_per_block * 4);
+    if (bph > 256) bph = 256;
+    const dim3 grid((unsigned)bph, (unsigned)BH);
+    if (d == 128)
+      hipLaunchKernelGGL(fa::fa_mx_rows_rot_kernel<128>, grid, dim3(256), 0, stream, x, signs,
+                         (uint8_t*)x_fp8, scales, N, post);
+    else
+      hipLaunchKernelGGL(fa::fa_mx_rows_rot_kernel<64>, grid, dim3(256), 0, stream, x, signs,
+                         (uint8_t*)x_fp8, scales, N, post);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_quantize_mxfp8_keys(const void* x, int in_dtype, void* x_fp8, unsigned char* scales,
+                                      int B, int H, int N, int d, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  const long long BH = (long long)B * H;
+  if (BH == 0 || N == 0) return FA_OK;
+  if (!x || !x_fp8 || !scales) return FA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_fp8) || !aligned4(scales)) return FA_ERR_ALIGN;
+  const int nkb = (int)ceil_div(N, 32);
+  const long long items = BH * nkb * (d / 4);
+  const long long grid = ceil_div(items, 256);
+  if (grid > INT_MAX) return FA_ERR_SHAPE;
+  const dim3 g((unsigned)grid), blk(256);
+  if (in_dtype == FA_DTYPE_BF16) {
+    if (d == 128)
+      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<true, 128>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales, N,
+                         nkb, items);
+    else
+      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<true, 64>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales, N,
+                         nkb, items);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<false, 128>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales,
+                         N, nkb, items);
+    else
+      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<false, 64>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales,
+                         N, nkb, items);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

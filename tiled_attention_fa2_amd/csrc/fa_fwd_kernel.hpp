@@ -87,6 +87,19 @@ __device__ __forceinline__ void mfma(const Operand<DT>& a, const Operand<DT>& b,
   }
 }
 
+// The fp8 MFMA with per-block scales. In this instruction lane half h, slot s
+// of an operand holds contraction index k = 32 (s / 16) + 16 h + s % 16, so
+// block b (k = 32b .. 32b + 31) is slots 16b .. 16b + 15 of both lane halves,
+// and its E8M0 scale for row i of A (column j of B) is byte OPA (OPB) of the
+// scale register of lane i + 32b (j + 32b).
+template <int OPA, int OPB>
+__device__ __forceinline__ void mfma_fp8_scaled(const Operand<kFP8>& a, const Operand<kFP8>& b,
+                                                f32x16& c, int scale_a, int scale_b) {
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                      __builtin_bit_cast(i32x8, b), c,
+                                                      0, 0, OPA, scale_a, OPB, scale_b);
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -112,6 +125,13 @@ struct FwdArgs {
   // BH / group key/value heads. group = 1 is ordinary multi-head attention.
   // FP8 descales: q at [bh], k at [BH + bh / group], v at [BH + BH / group + bh / group].
   int group;
+  // Per-block FP8 (kernels instantiated with MX): E8M0 scales, one byte
+  // (exponent + 127) per block of 32 elements along each product's
+  // contraction axis. q_scale [BH][N][D/32], k_scale [BH/group][N][D/32],
+  // v_scale [BH/group][ceil(N/32)][D].
+  const unsigned char* q_scale;
+  const unsigned char* k_scale;
+  const unsigned char* v_scale;
 };
 
 // Static shape of one instantiation.
@@ -755,6 +775,21 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, uint
                : "s"(m0), "v"(voff), "s"(r)
                : "memory", "m0");
 }
+// The same with 4 bytes per lane: lane L's dword at byte voff lands at LDS
+// address lds + 4 L (a dword past the end of the buffer reads as zero).
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t bytes, uint32_t lds, uint32_t voff) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  const int m0 = __builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -774,8 +809,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // NSTAGE LDS stages: tile j lives in stage j % NSTAGE and is fetched
 // NSTAGE - 1 tiles ahead. WPE = waves per SIMD the registers must allow.
+// MX: per-block FP8 (E8M0 scales applied by the MFMAs, see FwdArgs).
 template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2,
-          bool SPLIT = false>
+          bool SPLIT = false, bool MX = false>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int D = 128;
@@ -786,7 +822,13 @@ fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int NB = BN / 32, QK_STEPS = D / (2 * KPL), PV_STEPS = BN / (2 * KPL), MB = D / 32;
   constexpr int ROW = D * ES, CPR = ROW / 16;
   constexpr int TILE = BN * ROW;                 // bytes of one K or V tile
-  constexpr int STAGE = 2 * TILE;                // K tile, then V tile
+  // MX: the tile's K scales (BN keys x D/32) and V scales (BN/32 key blocks x
+  // D), one dword per lane of one DMA instruction each
+  constexpr int SC_K = MX ? BN * (D / 32) : 0;
+  constexpr int SC_V = MX ? (BN / 32) * D : 0;
+  static_assert(!MX || (DT == kFP8 && NSTAGE == 2 && SC_K == 256 && SC_V == 256),
+                "per-block scales: fp8, two stages, one 64-lane dword DMA per scale tile");
+  constexpr int STAGE = 2 * TILE + SC_K + SC_V;  // K tile, V tile, then the scales
   constexpr int NINSTR = TILE / 1024 / NWAVES;   // 1 KB DMA instructions per wave per tile
   constexpr int ROWS_PER_INSTR = 64 / CPR;
   static_assert(TILE % (1024 * NWAVES) == 0, "tile must split into whole DMA instructions");
@@ -819,7 +861,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
 
   float c = p.scale * 1.4426950408889634f;
   float dv = 1.0f;
-  if constexpr (DT == kFP8) {
+  if constexpr (DT == kFP8 && !MX) {
     c *= p.descales[bh] * p.descales[p.BH + bkv];
     dv = p.descales[p.BH + p.BH / p.group + bkv];
   }
@@ -836,17 +878,29 @@ fa_fwd_dma_kernel(FwdArgs p) {
   if (c == 0.0f) c = 1e-30f;
 
   Op qop[QK_STEPS];
+  // MX: lane half hh holds 16-byte chunks 4kk + 2x + hh of the row (the scaled
+  // MFMA's contraction order, so each hardware block is 32 consecutive head
+  // dims); otherwise chunks 4kk + 2hh + x (bf16: 2kk + hh). A and B use the
+  // same order, which is all the unscaled product needs.
+  int q_sc = 0;
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg, head_bytes);
-    const uint32_t qoff = (uint32_t)my_q * ROW + hh * KPL * ES;
+    const uint32_t qoff = (uint32_t)my_q * ROW + (MX ? 16 : KPL * ES) * hh;
 #pragma unroll
     for (int kk = 0; kk < QK_STEPS; ++kk)
 #pragma unroll
       for (int x = 0; x < Op::DW / 4; ++x) {
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kk * 2 * KPL * ES + 16 * x, 0, 0);
+        const uint32_t xo = MX ? 32 * x : 16 * x;
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + kk * 2 * KPL * ES + xo, 0, 0);
 #pragma unroll
         for (int y = 0; y < 4; ++y) qop[kk].w[4 * x + y] = w[y];
       }
+    if constexpr (MX) {
+      // the row's D/32 scale bytes; byte 2kk of q_sc is the block of step kk
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(p.q_scale + (size_t)bh * N * (D / 32), (uint32_t)N * (D / 32));
+      q_sc = (int)(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)my_q * (D / 32), 0, 0) >> (8 * hh));
+    }
     if (neg_scale) {
       constexpr uint32_t sign = ES == 2 ? 0x80008000u : 0x80808080u;
 #pragma unroll
@@ -889,6 +943,15 @@ fa_fwd_dma_kernel(FwdArgs p) {
       lds_dma16(Kg + g0, bytes, lds, k_goff);
       lds_dma16(Vg + g0, bytes, lds + TILE, v_goff);
     }
+    if constexpr (MX) {
+      if (wave == 0) {
+        const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_ptr)(st + 2 * TILE);
+        const int kb0 = kbase / 32, nkb = (N + 31) / 32;
+        lds_dma4(p.k_scale + ((size_t)bkv * N + kbase) * (D / 32), (uint32_t)(N - kbase) * (D / 32), lds,
+                 4 * lane);
+        lds_dma4(p.v_scale + ((size_t)bkv * nkb + kb0) * D, (uint32_t)(nkb - kb0) * D, lds + SC_K, 4 * lane);
+      }
+    }
   };
 
   // ---- MFMA operand read bases ----
@@ -897,7 +960,8 @@ fa_fwd_dma_kernel(FwdArgs p) {
   uint32_t kb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int lc = DT == kFP8 ? (4 * (u >> 1) + 2 * hh + (u & 1)) : (2 * u + hh);
+    const int lc = DT == kFP8 ? (MX ? 4 * (u >> 1) + 2 * (u & 1) + hh : 4 * (u >> 1) + 2 * hh + (u & 1))
+                              : (2 * u + hh);
     kb[u] = (uint32_t)l32 * ROW + 16 * (lc ^ gk);
   }
   // V (transpose reads): group g = lane / 16, j = lane % 16
@@ -968,7 +1032,16 @@ fa_fwd_dma_kernel(FwdArgs p) {
 #pragma unroll
             for (int y = 0; y < 4; ++y) a.w[4 * x + y] = w[y];
           }
-          mfma<DT>(a, qop[kk], s[b]);
+          if constexpr (MX) {
+            // the key row's D/32 scale bytes, block hh of step kk at byte 2kk
+            const int k_sc = (int)(*(const uint32_t*)(st + 2 * TILE + 4 * (32 * b + l32)) >> (8 * hh));
+            if (kk == 0)
+              mfma_fp8_scaled<0, 0>(a, qop[kk], s[b], k_sc, q_sc);
+            else
+              mfma_fp8_scaled<2, 2>(a, qop[kk], s[b], k_sc, q_sc);
+          } else {
+            mfma<DT>(a, qop[kk], s[b]);
+          }
         }
       if constexpr (LOOK > 0) interleave_reads_with_mfma<QK_STEPS * NB, kReadsPerOp, LOOK>();
 
@@ -1055,7 +1128,14 @@ fa_fwd_dma_kernel(FwdArgs p) {
               a.w[2 * t + 1] = (uint32_t)v2[1];
             }
           }
-          mfma<DT>(a, pop[n], oacc[mb]);
+          if constexpr (MX) {
+            // keys 64n + 32hh .. + 31 of the tile form block hh of this step;
+            // the scale of head dim 32mb + l32 in that key block; P unscaled
+            const int v_sc = st[2 * TILE + SC_K + (2 * n + hh) * D + 32 * mb + l32];
+            mfma_fp8_scaled<0, 0>(a, pop[n], oacc[mb], v_sc, 0x7F7F7F7F);
+          } else {
+            mfma<DT>(a, pop[n], oacc[mb]);
+          }
         }
     }
     // tile j+1 must have landed; with three stages tile j+2 may stay in flight

@@ -49,6 +49,10 @@ def lib() -> ctypes.CDLL:
         L.fa_quantize_fp8.restype = i
         L.fa_quantize_fp8_rotated.argtypes = [vp, i, vp, vp, vp, i, i, i, i, i, vp]
         L.fa_quantize_fp8_rotated.restype = i
+        L.fa_quantize_mxfp8_rows.argtypes = [vp, i, vp, i, vp, vp, i, i, i, i, vp]
+        L.fa_quantize_mxfp8_rows.restype = i
+        L.fa_quantize_mxfp8_keys.argtypes = [vp, i, vp, vp, i, i, i, i, vp]
+        L.fa_quantize_mxfp8_keys.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         sz = ctypes.c_size_t
@@ -64,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.fa_merge_partials.restype = i
         L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_fwd_gqa.restype = i
+        L.fa_fwd_mxfp8.argtypes = [vp] * 8 + [i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
+        L.fa_fwd_mxfp8.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -297,6 +303,101 @@ def quantize_qkv_fp8(q, k, v, signs=None):
         k8, _ = quantize_fp8_rotated(k, signs, False, descale=flat[B * H:B * H + B * Hkv])
     v8, _ = quantize_fp8(v, descale=flat[B * H + B * Hkv:])
     return q8, k8, v8, (flat.view(3, B * H) if Hkv == H else flat)
+
+
+def _float_code(x, name):
+    if not x.is_cuda or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, d] device tensor")
+    if x.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if x.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"{name} takes float32 or bfloat16")
+
+
+def quantize_mxfp8_rows(x, signs=None, fold_inverse_d: bool = False, out=None, scales=None):
+    """Per-block e4m3 quantisation of [B, H, N, d] rows in blocks of 32 head
+    dims (for Q and K), optionally after the randomised Hadamard rotation
+    (signs: int8 [d] device tensor; bfloat16 input) and a factor 1/d.
+    Returns (codes uint8 [B, H, N, d], E8M0 scales uint8 [B, H, N, d/32])."""
+    code = _float_code(x, "x")
+    B, H, N, d = x.shape
+    if signs is not None and (not signs.is_cuda or signs.dtype != torch.int8 or signs.dim() != 1
+                              or signs.numel() != d or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous int8 [d] device tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, N, max(d // 32, 1)), dtype=torch.uint8, device=x.device)
+    st = lib().fa_quantize_mxfp8_rows(_ptr(x), code, _ptr(signs), 1 if fold_inverse_d else 0, _ptr(out),
+                                      _ptr(scales), B, H, N, d, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_mxfp8_rows")
+    return out, scales
+
+
+def quantize_mxfp8_keys(x, out=None, scales=None):
+    """Per-block e4m3 quantisation of [B, H, N, d] in blocks of 32 keys of
+    one column (for V). Returns (codes uint8 [B, H, N, d], E8M0 scales uint8
+    [B, H, ceil(N/32), d])."""
+    code = _float_code(x, "x")
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (N + 31) // 32, d), dtype=torch.uint8, device=x.device)
+    st = lib().fa_quantize_mxfp8_keys(_ptr(x), code, _ptr(out), _ptr(scales), B, H, N, d, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_mxfp8_keys")
+    return out, scales
+
+
+def quantize_qkv_mxfp8(q, k, v, signs=None):
+    """Per-block quantisation of Q and K (row blocks) and V (key blocks).
+    With signs, Q and K are rotated first and 1/d goes into Q's values, so
+    fwd_mxfp8 on the result computes the same attention. Returns
+    (q8, k8, v8, (q_scales, k_scales, v_scales))."""
+    q8, qs = quantize_mxfp8_rows(q, signs=signs, fold_inverse_d=signs is not None)
+    k8, ks = quantize_mxfp8_rows(k, signs=signs)
+    v8, vs = quantize_mxfp8_keys(v)
+    return q8, k8, v8, (qs, ks, vs)
+
+
+def fwd_mxfp8(q, k, v, scales, causal: bool = False, scale: float | None = None, num_splits=None,
+              workspace=None, out=None, lse=None):
+    """FP8 forward on per-block codes (head dim 128). q: uint8 [B, Hq, N, d];
+    k, v: [B, Hkv, N, d]; scales: (q_scales [B, Hq, N, d/32], k_scales
+    [B, Hkv, N, d/32], v_scales [B, Hkv, ceil(N/32), d]) as the quantisers
+    return them. Returns (o bf16 [B, Hq, N, d], lse float32 [B, Hq, N])."""
+    _check_qkv(q, k, v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    qs, ks, vs = scales
+    for name, t, shape in (("q_scales", qs, (B, Hq, N, d // 32)), ("k_scales", ks, (B, Hkv, N, d // 32)),
+                           ("v_scales", vs, (B, Hkv, (N + 31) // 32, d))):
+        if not t.is_cuda or t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 {shape} device tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = default_splits(B, Hq, N, d, causal, DTYPE_FP8_E4M3)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if (o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous()
+            or tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("out must be bf16 [B, Hq, N, d] and lse float32 [B, Hq, N], contiguous")
+    ws_bytes = 0
+    if num_splits > 1:
+        ws_bytes = splitkv_workspace_bytes(B, Hq, N, d, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_mxfp8(_ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse),
+                            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), int(num_splits),
+                            _ptr(workspace) if num_splits > 1 else None, ws_bytes, _stream())
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_mxfp8")
+    return o, lse
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
