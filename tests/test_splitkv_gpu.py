@@ -84,7 +84,7 @@ def _check_split(q, k, v, dtype, causal, scale, S, label, rows=None, check_parts
             assert np.all(got_o[empty] == 0.0), (label, s)
             full = ~empty
             err_o = float(np.max(np.abs(got_o - O_s)[full], initial=0.0))
-            err_l = float(np.max(np.abs(got_l - L_s)[full], initial=0.0))
+            err_l = float(np.max(np.abs(got_l[full] - L_s[full]), initial=0.0))
             print(f"    chunk {s} keys [{s * chunk}, {min(N, (s + 1) * chunk)}) rows with keys "
                   f"{int(full.sum())}: max|dO|={err_o:.3e} max|dL|={err_l:.3e}", flush=True)
             assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_l[full]))
