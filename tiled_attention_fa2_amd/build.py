@@ -31,6 +31,8 @@ CEILING_SRC = os.path.join(ROOT, "tests", "hip", "mfma_ceiling.hip")
 CEILING_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_ceiling.so")
 VALU_SRC = os.path.join(ROOT, "tests", "hip", "valu_rates.hip")
 VALU_LIB = os.path.join(ROOT, "tests", "hip", "libvalu_rates.so")
+LDS_SRC = os.path.join(ROOT, "tests", "hip", "lds_rates.hip")
+LDS_LIB = os.path.join(ROOT, "tests", "hip", "liblds_rates.so")
 
 
 def _hipcc(cmd, verbose):
@@ -48,7 +50,7 @@ def build_probe(verbose: bool = False) -> str:
     tests."""
     _hipcc([HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_LIB + ".tmp"], verbose)
     os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
-    for src, lib in ((CEILING_SRC, CEILING_LIB), (VALU_SRC, VALU_LIB)):
+    for src, lib in ((CEILING_SRC, CEILING_LIB), (VALU_SRC, VALU_LIB), (LDS_SRC, LDS_LIB)):
         if os.path.exists(src):
             _hipcc([HIPCC, *FLAGS, src, "-o", lib + ".tmp"], verbose)
             os.replace(lib + ".tmp", lib)
