@@ -478,6 +478,14 @@ extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   return (size_t)8 * (size_t)B * (size_t)H * (size_t)N;
 }
 
+// 32-key blocks per wave of the dK/dV kernel (each wave reads its Q / dO
+// operands once for all of them): two at both head dims; at 128 the second
+// block's K/V operands are staged in LDS (its accumulators fill the registers)
+#ifndef FA_DKDV_KB
+#define FA_DKDV_KB 2
+#endif
+constexpr int kDkdvKB = FA_DKDV_KB;
+
 extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                       int d, int causal, float scale, int dtype, void* workspace,
@@ -516,26 +524,27 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.N = N;
   a.group = Hq / Hkv;
   a.n_tiles = (int)n_tiles;
+  a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * kDkdvKB);
   a.scale = scale;
   const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles)),
-      g_dkdv((unsigned)(BH / a.group * n_tiles));
+      g_dkdv((unsigned)(BH / a.group * a.n_ktiles));
   const bool c = causal != 0;
   if (d == 128) {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<128>, g_pre, blk, 0, stream, a);
     if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true>), g_dkdv, blk, 0, stream, a);
+      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true>), g_dq, blk, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false>), g_dkdv, blk, 0, stream, a);
+      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false>), g_dq, blk, 0, stream, a);
     }
   } else {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<64>, g_pre, blk, 0, stream, a);
     if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true>), g_dkdv, blk, 0, stream, a);
+      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true>), g_dq, blk, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false>), g_dkdv, blk, 0, stream, a);
+      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false>), g_dq, blk, 0, stream, a);
     }
   }

@@ -58,7 +58,8 @@ struct BwdArgs {
   int BH;               // batch * query heads
   int N;
   int group;            // query heads per key/value head
-  int n_tiles;          // 128-row tiles per head
+  int n_tiles;          // 128-row tiles per head (dQ kernel)
+  int n_ktiles;         // key tiles per head of the dK/dV kernel (128 KB keys each)
   float scale;
 };
 
@@ -334,16 +335,25 @@ fa_bwd_dq_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (batch * key/value head, 128 keys); waves own 32
-// keys and loop over the query tiles of every query head of their group.
-template <int D, bool CAUSAL>
+// dK, dV: one workgroup per (batch * key/value head, 128 KB keys); each wave
+// owns KB blocks of 32 keys and loops over the query tiles of every query head
+// of its group. The kernel is bound by its LDS reads (one wave per SIMD reads
+// at that SIMD's rate, and the transposed reads are the slow ones): with
+// KB = 2 every Q / dO operand read, row-major or transposed, feeds the MFMAs of
+// both key blocks, which halves the reads per flop. The K and V operands of
+// blocks b < KREG stay in registers; those of the others (when registers do not
+// suffice) in LDS, lane-major per operand, each lane reading back only what it
+// wrote (16 cheap row-major reads per tile and block, no bank conflicts).
+template <int D, bool CAUSAL, int KB, int KREG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(BwdArgs p) {
   using S = bwd::Shape<D>;
   using Op = Operand<kBF16>;
   constexpr int QK = S::QK_STEPS, PV = S::PV_STEPS, MB = S::MB, ROW = S::ROW, TILE = S::TILE;
   constexpr int STAGE = 2 * TILE + 1024;    // Q tile, dO tile, 32 (L2, D) pairs (1 KB slot)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  static_assert(KREG >= 1 && KREG <= KB, "at least one key block in registers");
+  constexpr int KVL_WAVE = (KB - KREG) * 2 * QK * 1024;   // staged K, V operands of one wave
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + bwd::kNWaves * KVL_WAVE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -351,30 +361,41 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
 
   const int BHkv = p.BH / p.group;
   int bkv, kt;
-  work_item(blockIdx.x, BHkv * p.n_tiles, p.n_tiles, 0, bkv, kt);
+  work_item(blockIdx.x, BHkv * p.n_ktiles, p.n_ktiles, 0, bkv, kt);
   const int N = p.N;
-  const int k0 = kt * bwd::kRows;
-  const int k0w = k0 + 32 * wave;
-  const int my_k = k0w + l32;
+  const int k0 = kt * bwd::kRows * KB;
+  const int k0w = k0 + 32 * KB * wave;      // the wave's first key; block b: k0w + 32 b
   const uint32_t head_bytes = (uint32_t)N * ROW;
   const unsigned char* Kg = (const unsigned char*)p.k + (size_t)bkv * head_bytes;
   const unsigned char* Vg = (const unsigned char*)p.v + (size_t)bkv * head_bytes;
   const float c = p.scale * 1.4426950408889634f;
 
-  // the wave's K and V rows: B operands of S = Q K^T and dP = dO V^T
-  Op kop[QK], vop[QK];
+  // the wave's K and V rows: B operands of S = Q K^T and dP = dO V^T; blocks
+  // b >= KREG go to the wave's LDS region: operand (b, K or V, kk) of lane l at
+  // ((b - KREG) * 2 QK + (K: 0, V: QK) + kk) * 1024 + 16 l
+  Op kop[KREG][QK], vop[KREG][QK];
+  unsigned char* kvl = smem + 2 * STAGE + wave * KVL_WAVE;
   {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, head_bytes);
-    const uint32_t off = (uint32_t)my_k * ROW + hh * 16;
 #pragma unroll
-    for (int kk = 0; kk < QK; ++kk) {
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 32, 0, 0);
-      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rv, off + kk * 32, 0, 0);
+    for (int b = 0; b < KB; ++b) {
+      const uint32_t off = (uint32_t)(k0w + 32 * b + l32) * ROW + hh * 16;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        kop[kk].w[y] = a[y];
-        vop[kk].w[y] = b[y];
+      for (int kk = 0; kk < QK; ++kk) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 32, 0, 0);
+        const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(rv, off + kk * 32, 0, 0);
+        if (b < KREG) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kop[b < KREG ? b : 0][kk].w[w] = x[w];
+            vop[b < KREG ? b : 0][kk].w[w] = y[w];
+          }
+        } else {
+          unsigned char* dst = kvl + ((b - KREG) * 2 * QK + kk) * 1024 + 16 * lane;
+          *(u32x4*)dst = x;
+          *(u32x4*)(dst + QK * 1024) = y;
+        }
       }
     }
   }
@@ -385,14 +406,16 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_ptr)smem;
   const bwd::ReadBases<D> rb(lane);
 
-  f32x16 dk[MB], dv[MB];
+  f32x16 dk[KB][MB], dv[KB][MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[mb][r] = 0.0f;
-      dv[mb][r] = 0.0f;
-    }
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[b][mb][r] = 0.0f;
+        dv[b][mb][r] = 0.0f;
+      }
 
   const int T = (N + 31) / 32;
   // causal: queries before the workgroup's first key see none of its keys
@@ -421,22 +444,47 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
       const int buf = (j - j_first) & 1;
       if (j + 1 < T) issue(j + 1, buf ^ 1);
       const int qbase = j * 32;
+      // causal: a tile entirely before the wave's first key contributes nothing
       const bool wave_active = !CAUSAL || qbase + 31 >= k0w;
       if (wave_active) {
         const unsigned char* st = smem + buf * STAGE;
-        f32x16 s, dp;
+        f32x16 s[KB], dp[KB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[r] = 0.0f;
-          dp[r] = 0.0f;
-        }
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[b][r] = 0.0f;
+            dp[b][r] = 0.0f;
+          }
 #pragma unroll
         for (int kk = 0; kk < QK; ++kk) {
-          Op a, b;
+          Op a, bo;
           bwd::read_rm<D>(st, rb, kk, a);
-          mfma<kBF16>(a, kop[kk], s);
-          bwd::read_rm<D>(st + TILE, rb, kk, b);
-          mfma<kBF16>(b, vop[kk], dp);
+#pragma unroll
+          for (int b = 0; b < KB; ++b) {
+            if (b < KREG) {
+              mfma<kBF16>(a, kop[b < KREG ? b : 0][kk], s[b]);
+            } else {
+              Op kl;
+              const u32x4 x = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + kk) * 1024 + 16 * lane);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) kl.w[w] = x[w];
+              mfma<kBF16>(a, kl, s[b]);
+            }
+          }
+          bwd::read_rm<D>(st + TILE, rb, kk, bo);
+#pragma unroll
+          for (int b = 0; b < KB; ++b) {
+            if (b < KREG) {
+              mfma<kBF16>(bo, vop[b < KREG ? b : 0][kk], dp[b]);
+            } else {
+              Op vl;
+              const u32x4 y = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + QK + kk) * 1024 + 16 * lane);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) vl.w[w] = y[w];
+              mfma<kBF16>(bo, vl, dp[b]);
+            }
+          }
         }
         // (L2, D) of the lane's 16 queries qbase + 8 (r / 4) + 4 hh + r % 4
         float l2[16], dd[16];
@@ -452,50 +500,60 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
           l2[4 * b4 + 3] = x1.z; dd[4 * b4 + 3] = x1.w;
         }
         // P = exp2(S c - L2), dS = P (dP - D); query qbase + 4hh + rel is
-        // valid iff it is < N and (causal) >= the lane's key
-        const bool need_mask = (qbase + 32 > N) || (CAUSAL && qbase < k0w + 31);
-        float pv[16], ds[16];
-        if (need_mask) {
-          asm volatile("" ::: "memory");
-          const int hi = N - qbase - 4 * hh;             // rel < hi
-          const int lo = CAUSAL ? my_k - qbase - 4 * hh : -(1 << 30);   // rel >= lo
+        // valid for key block b iff it is < N and (causal) >= the lane's key
+        const bool need_mask = (qbase + 32 > N) || (CAUSAL && qbase < k0w + 32 * KB - 1);
+        Op pop[KB][2], dsop[KB][2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rel = 8 * (r >> 2) + (r & 3);
-            const float t = (rel < hi && rel >= lo) ? __builtin_fmaf(s[r], c, -l2[r]) : -__builtin_inff();
-            pv[r] = __builtin_amdgcn_exp2f(t);
-            ds[r] = pv[r] * (dp[r] - dd[r]);
-          }
-        } else {
+        for (int b = 0; b < KB; ++b) {
+          float pv[16], ds[16];
+          if (need_mask) {
+            asm volatile("" ::: "memory");
+            const int hi = N - qbase - 4 * hh;                                          // rel < hi
+            const int lo = CAUSAL ? k0w + 32 * b + l32 - qbase - 4 * hh : -(1 << 30);   // rel >= lo
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-            ds[r] = pv[r] * (dp[r] - dd[r]);
+            for (int r = 0; r < 16; ++r) {
+              const int rel = 8 * (r >> 2) + (r & 3);
+              const float t = (rel < hi && rel >= lo) ? __builtin_fmaf(s[b][r], c, -l2[r]) : -__builtin_inff();
+              pv[r] = __builtin_amdgcn_exp2f(t);
+              ds[r] = pv[r] * (dp[b][r] - dd[r]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -l2[r]));
+              ds[r] = pv[r] * (dp[b][r] - dd[r]);
+            }
           }
+          bwd::pack_b(pv, pop[b]);
+          bwd::pack_b(ds, dsop[b]);
         }
-        Op pop[2], dsop[2];
-        bwd::pack_b(pv, pop);
-        bwd::pack_b(ds, dsop);
-        // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed)
+        // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed, once
+        // for all key blocks)
 #pragma unroll
         for (int n = 0; n < PV; ++n)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            Op a, b;
+            Op a, bq;
             bwd::read_tr<D>(st + TILE, rb, mb, n, a);
-            mfma<kBF16>(a, pop[n], dv[mb]);
-            bwd::read_tr<D>(st, rb, mb, n, b);
-            mfma<kBF16>(b, dsop[n], dk[mb]);
+#pragma unroll
+            for (int b = 0; b < KB; ++b) mfma<kBF16>(a, pop[b][n], dv[b][mb]);
+            bwd::read_tr<D>(st, rb, mb, n, bq);
+#pragma unroll
+            for (int b = 0; b < KB; ++b) mfma<kBF16>(bq, dsop[b][n], dk[b][mb]);
           }
       }
       wait_vmcnt<0>();
       __syncthreads();
     }
   }
-  if (my_k < N) {
-    const size_t row = (size_t)bkv * N + my_k;
-    bwd::store_rows<MB>(p.dk, row, hh, dk, p.scale);
-    bwd::store_rows<MB>(p.dv, row, hh, dv, 1.0f);
+#pragma unroll
+  for (int b = 0; b < KB; ++b) {
+    const int my_k = k0w + 32 * b + l32;
+    if (my_k < N) {
+      const size_t row = (size_t)bkv * N + my_k;
+      bwd::store_rows<MB>(p.dk, row, hh, dk[b], p.scale);
+      bwd::store_rows<MB>(p.dv, row, hh, dv[b], 1.0f);
+    }
   }
 }
 
