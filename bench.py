@@ -149,7 +149,16 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         r0 = (r0 + 128) % w.N
     dt = time.perf_counter() - t0
     flops = 4.0 * w.d * w.N * rows_done      # non-causal: every row sees N keys
+    if w.causal:
+        flops *= 0.5                         # the pages' convention: half the pairs
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{rows_done} query rows x all {w.N} keys (chunks of 128 rows, cycling heads) "
                       f"of {w.name}, fp64 numpy, {dt:.1f} s",
             "extrapolated_full_problem_s": dt * (w.B * w.H * w.N) / rows_done}
