@@ -9,8 +9,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = [os.path.join(PKG, "csrc", "fa_api.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("fa_api.hip", "fa_quant_api.hip", "fa_bwd_api.hip")]
 HEADERS = [os.path.join(ROOT, "include", "fa.h"),
+           os.path.join(PKG, "csrc", "fa_api_common.hpp"),
+           os.path.join(PKG, "csrc", "fa_bwd_kernel.hpp"),
            os.path.join(PKG, "csrc", "fa_fwd_kernel.hpp"),
            os.path.join(PKG, "csrc", "fa_merge_kernel.hpp"),
            os.path.join(PKG, "csrc", "fa_quant_kernel.hpp")]

@@ -1,17 +1,22 @@
-// C ABI of libfa.so: argument validation, choice of kernel instantiation, and
-// launch on the caller's stream. The declarations and the contract of every
-// entry point are in include/fa.h.
+// C ABI of libfa.so, forward part: argument validation, choice of kernel
+// instantiation, and launch on the caller's stream for the forward, split-KV
+// and merge entry points (the quantisers are in fa_quant_api.hip, the backward
+// in fa_bwd_api.hip). The declarations and the contract of every entry point
+// are in include/fa.h.
 #include <climits>
 #include <cmath>
 #include <cstdint>
 
 #include "fa.h"
-#include "fa_bwd_kernel.hpp"
+#include "fa_api_common.hpp"
 #include "fa_fwd_kernel.hpp"
 #include "fa_merge_kernel.hpp"
-#include "fa_quant_kernel.hpp"
 
 namespace {
+
+using fa_api::aligned16;
+using fa_api::aligned4;
+using fa_api::ceil_div;
 
 // Tile shapes: 4 waves x 32 query rows per workgroup; key tile 64 (bf16, fp8)
 // or 32 (fp32); registers bounded so two workgroups share a CU (2 waves per
@@ -94,8 +99,6 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
                 int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
                 const MxScales* mx, fa::FwdArgs& a, bool& empty);
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int Hkv, int N, int d, int causal, float scale, int dtype, const float* descales,
@@ -144,8 +147,6 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   }
   return FA_OK;
 }
-
-long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // Compute units of the current device, cached per device (0 if the query fails).
 int device_cus() {
@@ -321,232 +322,4 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   if (num_splits == 0) num_splits = -1;   // 0 selects the unsplit path inside run_fwd
   return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, num_splits,
                  workspace, workspace_bytes, stream);
-}
-
-extern "C" int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* descale,
-                               int B, int H, int N, int d, hipStream_t stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  const long long BH = (long long)B * H;
-  if (BH == 0) return FA_OK;
-  if (!descale) return FA_ERR_NULL;
-  if (BH > 65535) return FA_ERR_SHAPE;  // grid.y limit of the per-head kernels
-  if (N > 0 && (!x || !x_fp8)) return FA_ERR_NULL;
-  if (N > 0 && (!aligned16(x) || !aligned16(x_fp8))) return FA_ERR_ALIGN;
-  uint32_t* amax = reinterpret_cast<uint32_t*>(descale);
-  const int nbh = (int)BH;
-  const long long per_head = (long long)N * d;
-
-  hipLaunchKernelGGL(fa::fa_amax_clear, dim3((nbh + 255) / 256), dim3(256), 0, stream, amax, nbh);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  if (N > 0) {
-    // about 64 elements per thread per workgroup pass, at most 256 workgroups per head
-    long long bph = (per_head / 16 + 256 * 4 - 1) / (256 * 4);
-    if (bph < 1) bph = 1;
-    if (bph > 256) bph = 256;
-    const dim3 grid((unsigned)bph, (unsigned)nbh);
-    if (in_dtype == FA_DTYPE_BF16) {
-      hipLaunchKernelGGL(fa::fa_amax_kernel<true>, grid, dim3(256), 0, stream, x, amax, per_head);
-      hipLaunchKernelGGL(fa::fa_quant_kernel<true>, grid, dim3(256), 0, stream, x,
-                         (uint8_t*)x_fp8, (const uint32_t*)amax, per_head);
-    } else {
-      hipLaunchKernelGGL(fa::fa_amax_kernel<false>, grid, dim3(256), 0, stream, x, amax, per_head);
-      hipLaunchKernelGGL(fa::fa_quant_kernel<false>, grid, dim3(256), 0, stream, x,
-                         (uint8_t*)x_fp8, (const uint32_t*)amax, per_head);
-    }
-    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  }
-  hipLaunchKernelGGL(fa::fa_descale_finalize, dim3((nbh + 255) / 256), dim3(256), 0, stream, amax,
-                     nbh);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-extern "C" int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed char* signs,
-                                       void* x_fp8, float* descale, int B, int H, int N, int d,
-                                       int fold_inverse_d, hipStream_t stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  const long long BH = (long long)B * H;
-  if (BH == 0) return FA_OK;
-  if (!descale || !signs) return FA_ERR_NULL;
-  if (BH > 65535) return FA_ERR_SHAPE;  // grid.y limit of the per-head kernels
-  if (N > 0 && (!x || !x_fp8)) return FA_ERR_NULL;
-  if (N > 0 && (!aligned16(x) || !aligned16(x_fp8))) return FA_ERR_ALIGN;
-  uint32_t* amax = reinterpret_cast<uint32_t*>(descale);
-  const int nbh = (int)BH;
-
-  hipLaunchKernelGGL(fa::fa_amax_clear, dim3((nbh + 255) / 256), dim3(256), 0, stream, amax, nbh);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  if (N > 0) {
-    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
-    const int rows_per_block = 256 / (d / 8);
-    long long bph = ((long long)N + rows_per_block * 4 - 1) / (rows_per_block * 4);
-    if (bph > 256) bph = 256;
-    const dim3 grid((unsigned)bph, (unsigned)nbh);
-    if (d == 128) {
-      hipLaunchKernelGGL(fa::fa_rot_amax_kernel<128>, grid, dim3(256), 0, stream, x, signs, amax, N);
-      hipLaunchKernelGGL(fa::fa_rot_quant_kernel<128>, grid, dim3(256), 0, stream, x, signs,
-                         (uint8_t*)x_fp8, (const uint32_t*)amax, N);
-    } else {
-      hipLaunchKernelGGL(fa::fa_rot_amax_kernel<64>, grid, dim3(256), 0, stream, x, signs, amax, N);
-      hipLaunchKernelGGL(fa::fa_rot_quant_kernel<64>, grid, dim3(256), 0, stream, x, signs,
-                         (uint8_t*)x_fp8, (const uint32_t*)amax, N);
-    }
-    if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  }
-  const float post = fold_inverse_d ? 1.0f / (float)d : 1.0f;
-  hipLaunchKernelGGL(fa::fa_descale_finalize_scaled, dim3((nbh + 255) / 256), dim3(256), 0, stream,
-                     amax, nbh, post);
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-extern "C" int fa_quantize_mxfp8_rows(const void* x, int in_dtype, const signed char* signs,
-                                      int fold_inverse_d, void* x_fp8, unsigned char* scales, int B,
-                                      int H, int N, int d, hipStream_t stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (signs && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  const long long BH = (long long)B * H;
-  if (BH == 0 || N == 0) return FA_OK;
-  if (!x || !x_fp8 || !scales) return FA_ERR_NULL;
-  if (!aligned16(x) || !aligned16(x_fp8)) return FA_ERR_ALIGN;
-  const float post = fold_inverse_d ? 1.0f / (float)d : 1.0f;
-  if (!signs) {
-    const long long nblocks = BH * N * (d / 32);
-    const long long grid = ceil_div(nblocks, 256);
-    if (grid > INT_MAX) return FA_ERR_SHAPE;
-    if (in_dtype == FA_DTYPE_BF16)
-      hipLaunchKernelGGL(fa::fa_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                         (uint8_t*)x_fp8, scales, nblocks, post);
-    else
-      hipLaunchKernelGGL(fa::fa_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                         (uint8_t*)x_fp8, scales, nblocks, post);
-  } else {
-    if (BH > 65535) return FA_ERR_SHAPE;   // grid.y limit of the per-head kernel
-    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
-    const int rows_per_block = 256 / (d / 8);
-    long long bph = ceil_div(N, rows_per_block * 4);
-    if (bph > 256) bph = 256;
-    const dim3 grid((unsigned)bph, (unsigned)BH);
-    if (d == 128)
-      hipLaunchKernelGGL(fa::fa_mx_rows_rot_kernel<128>, grid, dim3(256), 0, stream, x, signs,
-                         (uint8_t*)x_fp8, scales, N, post);
-    else
-      hipLaunchKernelGGL(fa::fa_mx_rows_rot_kernel<64>, grid, dim3(256), 0, stream, x, signs,
-                         (uint8_t*)x_fp8, scales, N, post);
-  }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-extern "C" int fa_quantize_mxfp8_keys(const void* x, int in_dtype, void* x_fp8, unsigned char* scales,
-                                      int B, int H, int N, int d, hipStream_t stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  const long long BH = (long long)B * H;
-  if (BH == 0 || N == 0) return FA_OK;
-  if (!x || !x_fp8 || !scales) return FA_ERR_NULL;
-  if (!aligned16(x) || !aligned16(x_fp8) || !aligned4(scales)) return FA_ERR_ALIGN;
-  const int nkb = (int)ceil_div(N, 32);
-  const long long items = BH * nkb * (d / 4);
-  const long long grid = ceil_div(items, 256);
-  if (grid > INT_MAX) return FA_ERR_SHAPE;
-  const dim3 g((unsigned)grid), blk(256);
-  if (in_dtype == FA_DTYPE_BF16) {
-    if (d == 128)
-      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<true, 128>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales, N,
-                         nkb, items);
-    else
-      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<true, 64>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales, N,
-                         nkb, items);
-  } else {
-    if (d == 128)
-      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<false, 128>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales,
-                         N, nkb, items);
-    else
-      hipLaunchKernelGGL((fa::fa_mx_keys_kernel<false, 64>), g, blk, 0, stream, x, (uint8_t*)x_fp8, scales,
-                         N, nkb, items);
-  }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
-extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int N) {
-  if (B < 0 || H < 0 || N < 0) return 0;
-  return (size_t)8 * (size_t)B * (size_t)H * (size_t)N;
-}
-
-// 32-key blocks per wave of the dK/dV kernel (each wave reads its Q / dO
-// operands once for all of them): two at both head dims; at 128 the second
-// block's K/V operands are staged in LDS (its accumulators fill the registers)
-#ifndef FA_DKDV_KB
-#define FA_DKDV_KB 2
-#endif
-constexpr int kDkdvKB = FA_DKDV_KB;
-
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                      int d, int causal, float scale, int dtype, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-  if (B < 0 || Hq < 0 || N < 0) return FA_ERR_SHAPE;
-  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0)) return FA_ERR_SHAPE;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
-  if (!std::isfinite(scale)) return FA_ERR_SCALE;
-  const long long BH = (long long)B * Hq;
-  if (BH == 0 || N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_ALIGN;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < fa_bwd_workspace_bytes(B, Hq, N))
-    return FA_ERR_WORKSPACE;
-  const long long n_tiles = ceil_div(N, fa::bwd::kRows);
-  if (BH > INT_MAX || BH * n_tiles > INT_MAX) return FA_ERR_SHAPE;
-  if (((long long)N + 128) * d * 2 > INT_MAX) return FA_ERR_SHAPE;
-  const long long pre_blocks = ceil_div(BH * N, 256 / (d / 8));
-  if (pre_blocks > INT_MAX) return FA_ERR_SHAPE;
-
-  fa::BwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.ld = static_cast<float2*>(workspace);
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.BH = (int)BH;
-  a.N = N;
-  a.group = Hq / Hkv;
-  a.n_tiles = (int)n_tiles;
-  a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * kDkdvKB);
-  a.scale = scale;
-  const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles)),
-      g_dkdv((unsigned)(BH / a.group * a.n_ktiles));
-  const bool c = causal != 0;
-  if (d == 128) {
-    hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<128>, g_pre, blk, 0, stream, a);
-    if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true>), g_dq, blk, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false>), g_dq, blk, 0, stream, a);
-    }
-  } else {
-    hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<64>, g_pre, blk, 0, stream, a);
-    if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true>), g_dq, blk, 0, stream, a);
-    } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false>), g_dq, blk, 0, stream, a);
-    }
-  }
-  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
