@@ -140,6 +140,7 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
   a.causal = causal ? 1 : 0;
   a.scale = scale;
   a.group = H / Hkv;
+  a.causal_order = fa_api::causal_order(BH, a.group, N, d, es);
   if (mx) {
     a.q_scale = mx->q;
     a.k_scale = mx->k;

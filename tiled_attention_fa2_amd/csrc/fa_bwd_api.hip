@@ -65,6 +65,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.group = Hq / Hkv;
   a.n_tiles = (int)n_tiles;
   a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * kDkdvKB);
+  a.causal_order = fa_api::causal_order(BH, a.group, N, d, 2);
   a.scale = scale;
   const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles)),
       g_dkdv((unsigned)(BH / a.group * a.n_ktiles));

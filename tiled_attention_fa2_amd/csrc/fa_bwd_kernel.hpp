@@ -60,6 +60,7 @@ struct BwdArgs {
   int group;            // query heads per key/value head
   int n_tiles;          // 128-row tiles per head (dQ kernel)
   int n_ktiles;         // key tiles per head of the dK/dV kernel (128 KB keys each)
+  int causal_order;     // order of the dQ kernel's causal tiles (work_item)
   float scale;
 };
 
@@ -213,7 +214,7 @@ fa_bwd_dq_kernel(BwdArgs p) {
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
   int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_tiles, p.n_tiles, CAUSAL ? 1 : 0, bh, qt);
+  work_item(blockIdx.x, p.BH * p.n_tiles, p.n_tiles, CAUSAL ? p.causal_order : 0, bh, qt);
   const int N = p.N;
   const int q0 = qt * bwd::kRows;
   const int q0w = q0 + 32 * wave;

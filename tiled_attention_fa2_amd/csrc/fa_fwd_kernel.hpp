@@ -111,6 +111,9 @@ struct FwdArgs {
   int N;
   int n_qtiles;
   int causal;
+  // Order of causal work items (work_item): 1 = head by head, 2 = longest
+  // query tiles first across the heads each XCD holds. Chosen by the host.
+  int causal_order;
   float scale;
   // Split-KV mode (kernels instantiated with SPLIT): split s of a query tile
   // takes the keys [s * split_keys, (s + 1) * split_keys) and writes its
@@ -218,11 +221,22 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 // the 8 XCDs; this remap hands every XCD a contiguous range of logical items,
 // so the query tiles resident on one XCD share a head and its K/V stream
 // through that XCD's L2. Logical items run head by head; within a head, causal
-// tiles go longest first.
+// tiles go longest first (causal = 1). With causal = 2 and whole heads per
+// XCD (heads a multiple of 8), the XCD's items go longest first across all of
+// its heads (the longest tile of every head, then the next, ...), so no long
+// tile of a late head starts while the rest of the XCD is draining; the host
+// picks it when those heads' K/V are small enough to share the caches.
 __host__ __device__ __forceinline__ void work_item(int bid, int total, int n_qtiles, int causal,
                                           int& bh, int& qt) {
   const int per = total >> 3, rem = total & 7;
   const int xcd = bid & 7, slot = bid >> 3;
+  if (causal == 2 && rem == 0 && per % n_qtiles == 0) {
+    const int heads = per / n_qtiles;
+    const int rank = slot / heads;   // 0: the longest tile
+    bh = xcd * heads + (slot - rank * heads);
+    qt = n_qtiles - 1 - rank;
+    return;
+  }
   const int lin = (xcd < rem) ? xcd * (per + 1) + slot
                               : rem * (per + 1) + (xcd - rem) * per + slot;
   bh = lin / n_qtiles;
@@ -377,7 +391,7 @@ fa_fwd_kernel(FwdArgs p) {
   const int hh = lane >> 5;
 
   int bh, qt, sp;
-  split_item<SPLIT, BN>(p, CAUSAL ? 1 : 0, bh, qt, sp);
+  split_item<SPLIT, BN>(p, CAUSAL ? p.causal_order : 0, bh, qt, sp);
   const int N = p.N;
   const int q0 = qt * C::BM;
   const int q0w = q0 + 32 * wave;
@@ -845,7 +859,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
   const int hh = lane >> 5;
 
   int bh, qt, sp;
-  split_item<SPLIT, BN>(p, CAUSAL ? 1 : 0, bh, qt, sp);
+  split_item<SPLIT, BN>(p, CAUSAL ? p.causal_order : 0, bh, qt, sp);
   const int N = p.N;
   const int q0 = qt * BM;
   const int q0w = q0 + 32 * wave;
