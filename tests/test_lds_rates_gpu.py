@@ -1,6 +1,6 @@
 """LDS read throughput of the attention kernels' read patterns on one MI355X
-CU (tests/hip/lds_rates.hip): the measurement behind the statement that the
-backward's dK/dV kernel, with one wave per SIMD, is bound by its LDS reads.
+CU (tests/hip/lds_rates.hip): what a wave's operand reads cost at the
+backward's one wave per SIMD and at the forward's occupancy.
 
 Patterns (32-row tiles of 256-byte bf16 rows, 16-byte chunks XOR-swizzled):
   * row-major ds_read_b128: lane = row l32, logical chunk 2u + hh, swizzle

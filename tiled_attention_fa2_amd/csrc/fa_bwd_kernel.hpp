@@ -338,10 +338,11 @@ fa_bwd_dq_kernel(BwdArgs p) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (batch * key/value head, 128 KB keys); each wave
 // owns KB blocks of 32 keys and loops over the query tiles of every query head
-// of its group. The kernel is bound by its LDS reads (one wave per SIMD reads
-// at that SIMD's rate, and the transposed reads are the slow ones): with
-// KB = 2 every Q / dO operand read, row-major or transposed, feeds the MFMAs of
-// both key blocks, which halves the reads per flop. The K and V operands of
+// of its group. The kernel waits on its LDS reads: at one wave per SIMD with
+// every register taken, one operand pair is in flight at a time and each pair
+// of MFMAs waits for the reads before it. With KB = 2 every Q / dO operand
+// read, row-major or transposed, feeds the MFMAs of both key blocks, which
+// halves the read-and-wait rounds per flop. The K and V operands of
 // blocks b < KREG stay in registers; those of the others (when registers do not
 // suffice) in LDS, lane-major per operand, each lane reading back only what it
 // wrote (16 cheap row-major reads per tile and block, no bank conflicts).
