@@ -672,7 +672,10 @@ fa_fwd_kernel(FwdArgs p) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int r0 = n * KPL + 4 * w;
-            int v = 0;
+            // both halves are overwritten below: an opaque, unset word spares the
+            // v_mov that clearing it would cost
+            int v;
+            asm volatile("" : "=v"(v));
             v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15],
                                                 s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
             v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15],
@@ -977,6 +980,9 @@ fa_fwd_dma_kernel(FwdArgs p) {
     const int lc = DT == kFP8 ? (MX ? 4 * (u >> 1) + 2 * (u & 1) + hh : 4 * (u >> 1) + 2 * hh + (u & 1))
                               : (2 * u + hh);
     kb[u] = (uint32_t)l32 * ROW + 16 * (lc ^ gk);
+    // one register per base: left visible, the compiler splits it into a row
+    // part and a chunk part and spends two VALU ops per base and tile
+    asm volatile("" : "+v"(kb[u]));
   }
   // V (transpose reads): group g = lane / 16, j = lane % 16
   const int vg = lane >> 4, vj = lane & 15, va = vg & 1;
@@ -1111,7 +1117,10 @@ fa_fwd_dma_kernel(FwdArgs p) {
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int r0 = n * KPL + 4 * w;
-            int v = 0;
+            // both halves are overwritten below: an opaque, unset word spares the
+            // v_mov that clearing it would cost
+            int v;
+            asm volatile("" : "=v"(v));
             v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
             v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15], s[(r0 + 3) >> 4][(r0 + 3) & 15], v, true);
             pop[n].w[w] = (uint32_t)v;
