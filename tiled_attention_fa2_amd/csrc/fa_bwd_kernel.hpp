@@ -153,6 +153,23 @@ __device__ __forceinline__ void read_tr(const unsigned char* tile, const ReadBas
   }
 }
 
+// Scheduling order of a phase of STEPS steps, each R LDS reads feeding M
+// MFMAs: the reads of the first LOOK steps, then the MFMAs of one step and the
+// reads LOOK steps ahead, and so on. At one wave per SIMD nothing else hides an
+// LDS read's latency, and left to itself the compiler issues each step's reads
+// right before the MFMAs that need them.
+template <int STEPS, int R, int M, int LOOK>
+__device__ __forceinline__ void pipeline_reads() {
+  static_assert(LOOK >= 1 && LOOK < STEPS, "look-ahead inside the phase");
+  __builtin_amdgcn_sched_group_barrier(0x100, LOOK * R, 0);
+#pragma unroll
+  for (int i = 0; i < STEPS - LOOK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LOOK * M, 0);
+}
+
 // One 32-row tile of a [N][D] bf16 head (rows from r_first; rows >= N read as
 // zero) into LDS at `lds` by DMA: every wave issues NINSTR instructions.
 template <int D>
@@ -199,6 +216,11 @@ __device__ __forceinline__ void store_rows(void* out, size_t row, int hh, const 
 }  // namespace bwd
 
 // ---------------------------------------------------------------------------
+#ifndef FA_DQ_LOOK
+#define FA_DQ_LOOK 2
+#endif
+constexpr int kDqLook = FA_DQ_LOOK;   // MFMA steps of LDS reads in flight
+
 // dQ: one workgroup per (batch * query head, 128 queries); waves own 32 rows.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -293,6 +315,7 @@ fa_bwd_dq_kernel(BwdArgs p) {
         bwd::read_rm<D>(st + TILE, rb, kk, b);
         mfma<kBF16>(b, dop[kk], dpt);
       }
+      bwd::pipeline_reads<QK, 2, 2, kDqLook>();
       // P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D); key kbase + 4hh + rel
       const bool need_mask = (kbase + 32 > N) || (CAUSAL && kbase + 31 > q0w);
       float ds[16];
@@ -328,6 +351,7 @@ fa_bwd_dq_kernel(BwdArgs p) {
           bwd::read_tr<D>(st, rb, mb, n, a);
           mfma<kBF16>(a, dsop[n], dq[mb]);
         }
+      bwd::pipeline_reads<PV * MB, 2, 1, kDqLook>();
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -346,6 +370,11 @@ fa_bwd_dq_kernel(BwdArgs p) {
 // blocks b < KREG stay in registers; those of the others (when registers do not
 // suffice) in LDS, lane-major per operand, each lane reading back only what it
 // wrote (16 cheap row-major reads per tile and block, no bank conflicts).
+#ifndef FA_DKDV_LOOK
+#define FA_DKDV_LOOK 2
+#endif
+constexpr int kDkdvLook = FA_DKDV_LOOK;   // MFMA steps of LDS reads in flight
+
 template <int D, bool CAUSAL, int KB, int KREG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(BwdArgs p) {
@@ -488,6 +517,7 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
             }
           }
         }
+        bwd::pipeline_reads<QK, 2 + 2 * (KB - KREG), 2 * KB, kDkdvLook>();
         // (L2, D) of the lane's 16 queries qbase + 8 (r / 4) + 4 hh + r % 4
         float l2[16], dd[16];
         const float* ldt = (const float*)(st + 2 * TILE);
@@ -543,6 +573,7 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
             for (int b = 0; b < KB; ++b) mfma<kBF16>(bq, dsop[b][n], dk[b][mb]);
           }
+        bwd::pipeline_reads<PV * MB, 4, 2 * KB, kDkdvLook>();
       }
       wait_vmcnt<0>();
       __syncthreads();
