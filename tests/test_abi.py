@@ -292,3 +292,16 @@ def test_bwd_validation_codes(lib, kw, code):
 def test_bwd_workspace_bytes(lib):
     assert fa.bwd_workspace_bytes(2, 3, 100) == 8 * 2 * 3 * 100
     assert fa.bwd_workspace_bytes(-1, 3, 100) == 0
+
+
+def test_binding_rejects_host_tensors_before_any_launch():
+    import torch
+
+    x = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.quantize_fp8(x)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)
+    assert fa._device(None, None) is None
+    with pytest.raises(ValueError, match="device tensor"):
+        fa._device(None, x)

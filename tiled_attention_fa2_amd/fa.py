@@ -86,8 +86,26 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+def _device(*tensors) -> torch.device:
+    """The one device every given tensor (None entries skipped) lives on."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+    return dev
+
+
+def _call(name: str, dev: torch.device, *args) -> int:
+    """Enqueue a library entry point on `dev`: that device current, on its
+    current torch stream (the last argument of every enqueuing entry point)."""
+    with torch.cuda.device(dev):
+        return getattr(lib(), name)(*args, torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -124,10 +142,12 @@ def splitkv_workspace_bytes(B: int, H: int, N: int, d: int, num_splits: int) -> 
     return int(lib().fa_splitkv_workspace_bytes(int(B), int(H), int(N), int(d), int(num_splits)))
 
 
-def default_splits(B: int, H: int, N: int, d: int, causal: bool, dtype_code: int) -> int:
-    """The number of key chunks the library picks for this shape on the current device."""
-    return int(lib().fa_splitkv_default_splits(int(B), int(H), int(N), int(d),
-                                               1 if causal else 0, int(dtype_code)))
+def default_splits(B: int, H: int, N: int, d: int, causal: bool, dtype_code: int, device=None) -> int:
+    """The number of key chunks the library picks for this shape on `device`
+    (default: the current device)."""
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        return int(lib().fa_splitkv_default_splits(int(B), int(H), int(N), int(d),
+                                                   1 if causal else 0, int(dtype_code)))
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None,
@@ -169,21 +189,22 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
                              "B*Hq + 2*B*Hkv values")
     ds = _ptr(descales) if code == DTYPE_FP8_E4M3 else None
     if num_splits is None:
-        num_splits = default_splits(B, H, N, d, causal, code)
+        num_splits = default_splits(B, H, N, d, causal, code, q.device)
     if Hkv != H:
         need = splitkv_workspace_bytes(B, H, N, d, num_splits) if num_splits > 1 else 0
         if num_splits > 1 and workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-        st = lib().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d,
-                              1 if causal else 0, float(scale), code, ds, int(num_splits),
-                              _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                              _stream())
+        dev = _device(q, k, v, out, lse, descales, workspace)
+        st = _call("fa_fwd_gqa", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d,
+                   1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace),
+                   0 if workspace is None else workspace.numel())
         if st != FA_OK:
             raise FAError(st, "fa_fwd_gqa")
         return out, lse
     if num_splits == 1 and workspace is None:
-        st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                          1 if causal else 0, float(scale), code, ds, _stream())
+        dev = _device(q, k, v, out, lse, descales)
+        st = _call("fa_fwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                   1 if causal else 0, float(scale), code, ds)
         if st != FA_OK:
             raise FAError(st, "fa_fwd")
         return out, lse
@@ -192,9 +213,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 device tensor")
-    st = lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                              1 if causal else 0, float(scale), code, ds, int(num_splits),
-                              _ptr(workspace), workspace.numel(), _stream())
+    dev = _device(q, k, v, out, lse, descales, workspace)
+    st = _call("fa_fwd_splitkv", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+               1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace),
+               workspace.numel())
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
     return out, lse
@@ -229,8 +251,9 @@ def merge_partials(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=N
         out = torch.empty((BH, N, d), dtype=out_dtype, device=o_parts.device)
     if lse is None:
         lse = torch.empty((BH, N), dtype=torch.float32, device=o_parts.device)
-    st = lib().fa_merge_partials(_ptr(o_parts), _ptr(lse_parts), S, 1, BH, N, d, code,
-                                 _ptr(out), _ptr(lse), _stream())
+    dev = _device(o_parts, lse_parts, out, lse)
+    st = _call("fa_merge_partials", dev, _ptr(o_parts), _ptr(lse_parts), S, 1, BH, N, d, code, _ptr(out),
+               _ptr(lse))
     if st != FA_OK:
         raise FAError(st, "fa_merge_partials")
     return out, lse
@@ -253,7 +276,8 @@ def quantize_fp8(x, out=None, descale=None):
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
-    st = lib().fa_quantize_fp8(_ptr(x), code, _ptr(out), _ptr(descale), B, H, N, d, _stream())
+    dev = _device(x, out, descale)
+    st = _call("fa_quantize_fp8", dev, _ptr(x), code, _ptr(out), _ptr(descale), B, H, N, d)
     if st != FA_OK:
         raise FAError(st, "fa_quantize_fp8")
     return out, descale
@@ -277,8 +301,9 @@ def quantize_fp8_rotated(x, signs, fold_inverse_d: bool, out=None, descale=None)
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
-    st = lib().fa_quantize_fp8_rotated(_ptr(x), DTYPE_BF16, _ptr(signs), _ptr(out), _ptr(descale),
-                                       B, H, N, d, 1 if fold_inverse_d else 0, _stream())
+    dev = _device(x, signs, out, descale)
+    st = _call("fa_quantize_fp8_rotated", dev, _ptr(x), DTYPE_BF16, _ptr(signs), _ptr(out), _ptr(descale), B,
+               H, N, d, 1 if fold_inverse_d else 0)
     if st != FA_OK:
         raise FAError(st, "fa_quantize_fp8_rotated")
     return out, descale
@@ -329,8 +354,9 @@ def quantize_mxfp8_rows(x, signs=None, fold_inverse_d: bool = False, out=None, s
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, N, max(d // 32, 1)), dtype=torch.uint8, device=x.device)
-    st = lib().fa_quantize_mxfp8_rows(_ptr(x), code, _ptr(signs), 1 if fold_inverse_d else 0, _ptr(out),
-                                      _ptr(scales), B, H, N, d, _stream())
+    dev = _device(x, signs, out, scales)
+    st = _call("fa_quantize_mxfp8_rows", dev, _ptr(x), code, _ptr(signs), 1 if fold_inverse_d else 0,
+               _ptr(out), _ptr(scales), B, H, N, d)
     if st != FA_OK:
         raise FAError(st, "fa_quantize_mxfp8_rows")
     return out, scales
@@ -346,7 +372,8 @@ def quantize_mxfp8_keys(x, out=None, scales=None):
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, (N + 31) // 32, d), dtype=torch.uint8, device=x.device)
-    st = lib().fa_quantize_mxfp8_keys(_ptr(x), code, _ptr(out), _ptr(scales), B, H, N, d, _stream())
+    dev = _device(x, out, scales)
+    st = _call("fa_quantize_mxfp8_keys", dev, _ptr(x), code, _ptr(out), _ptr(scales), B, H, N, d)
     if st != FA_OK:
         raise FAError(st, "fa_quantize_mxfp8_keys")
     return out, scales
@@ -380,7 +407,7 @@ def fwd_mxfp8(q, k, v, scales, causal: bool = False, scale: float | None = None,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
-        num_splits = default_splits(B, Hq, N, d, causal, DTYPE_FP8_E4M3)
+        num_splits = default_splits(B, Hq, N, d, causal, DTYPE_FP8_E4M3, q.device)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
@@ -392,9 +419,10 @@ def fwd_mxfp8(q, k, v, scales, causal: bool = False, scale: float | None = None,
         ws_bytes = splitkv_workspace_bytes(B, Hq, N, d, num_splits)
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    st = lib().fa_fwd_mxfp8(_ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(o), _ptr(lse),
-                            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), int(num_splits),
-                            _ptr(workspace) if num_splits > 1 else None, ws_bytes, _stream())
+    dev = _device(q, k, v, qs, ks, vs, o, lse, workspace)
+    st = _call("fa_fwd_mxfp8", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(o),
+               _ptr(lse), B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), int(num_splits),
+               _ptr(workspace) if num_splits > 1 else None, ws_bytes)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_mxfp8")
     return o, lse
@@ -430,9 +458,10 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
             raise ValueError(f"{name} has the wrong dtype, shape or layout")
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
-    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                      _ptr(dv), B, H, Hkv, N, d, 1 if causal else 0, float(scale), DTYPE_BF16,
-                      _ptr(workspace), workspace.numel(), _stream())
+    dev = _device(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    st = _call("fa_bwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+               _ptr(dv), B, H, Hkv, N, d, 1 if causal else 0, float(scale), DTYPE_BF16, _ptr(workspace),
+               workspace.numel())
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
