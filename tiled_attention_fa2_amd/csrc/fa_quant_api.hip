@@ -70,9 +70,9 @@ extern "C" int fa_quantize_fp8_rotated(const void* x, int in_dtype, const signed
   hipLaunchKernelGGL(fa::fa_amax_clear, dim3((nbh + 255) / 256), dim3(256), 0, stream, amax, nbh);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   if (N > 0) {
-    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
-    const int rows_per_block = 256 / (d / 8);
-    long long bph = ((long long)N + rows_per_block * 4 - 1) / (rows_per_block * 4);
+    // d/32 lanes per row; about 2 rows per lane, at most 256 workgroups per head
+    const int rows_per_block = 256 / (d / 32);
+    long long bph = ((long long)N + rows_per_block * 2 - 1) / (rows_per_block * 2);
     if (bph > 256) bph = 256;
     const dim3 grid((unsigned)bph, (unsigned)nbh);
     if (d == 128) {
@@ -116,9 +116,9 @@ extern "C" int fa_quantize_mxfp8_rows(const void* x, int in_dtype, const signed 
                          (uint8_t*)x_fp8, scales, nblocks, post);
   } else {
     if (BH > 65535) return FA_ERR_SHAPE;   // grid.y limit of the per-head kernel
-    // d/8 lanes per row; about 4 rows per lane, at most 256 workgroups per head
-    const int rows_per_block = 256 / (d / 8);
-    long long bph = ceil_div(N, rows_per_block * 4);
+    // d/32 lanes per row; about 2 rows per lane, at most 256 workgroups per head
+    const int rows_per_block = 256 / (d / 32);
+    long long bph = ceil_div(N, rows_per_block * 2);
     if (bph > 256) bph = 256;
     const dim3 grid((unsigned)bph, (unsigned)BH);
     if (d == 128)

@@ -121,59 +121,94 @@ __global__ void __launch_bounds__(256) fa_quant_kernel(const void* x, uint8_t* o
 // partial sum of at most d signed bf16 values is exact there (unless a row
 // spans more than 38 binary orders of magnitude), so y is the exact sum
 // rounded once to fp32 whatever the order. Each row of D bf16 is handled by
-// D/8 consecutive lanes holding 8 consecutive elements each: butterflies of
-// stride 1, 2, 4 inside a lane, 8..D/2 across lanes.
-template <int D>
-__device__ __forceinline__ void rotate_row8(const void* x, size_t e0, const signed char* signs, int c,
-                                            float* y) {
-  const qu32x4 w = *(const qu32x4*)((const unsigned short*)x + e0);
-  double v[8];
+// D/32 consecutive lanes (a quarter or half of a DPP quad) holding 32
+// consecutive elements each: butterflies of stride 1..16 inside a lane,
+// strides 32 and 64 between the lanes of the quad with DPP quad permutes (no
+// LDS traffic). Every butterfly is one v_fma_f64 with a weight of +-1, exact.
+
+// Sign masks of lane c, one per bf16 pair: word j has bit 15 set when
+// element 32c + 2j is negated and bit 31 when element 32c + 2j + 1 is, so one
+// XOR with the loaded pair applies both signs.
+struct RotSigns {
+  uint32_t w[16];
+};
+__device__ __forceinline__ RotSigns rot_sign_mask(const signed char* signs, int c) {
+  RotSigns m;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[2 * k] = (double)q_u2f(w[k] << 16);
-    v[2 * k + 1] = (double)q_u2f(w[k] & 0xffff0000u);
+  for (int j = 0; j < 16; ++j)
+    m.w[j] = (signs[32 * c + 2 * j] < 0 ? 0x8000u : 0u) | (signs[32 * c + 2 * j + 1] < 0 ? 0x80000000u : 0u);
+  return m;
+}
+
+// v from the lane that differs in bit M of its quad position (M = 1 or 2)
+template <int M>
+__device__ __forceinline__ double quad_xor(double v) {
+  static_assert(M == 1 || M == 2, "quad permutes only");
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// y[t] = element 32c + t of the rotated row whose bf16 elements 32c .. 32c+31
+// start at element e0 of x (lane c of the row's D/32 lanes)
+template <int D>
+__device__ __forceinline__ void rotate_row32(const void* x, size_t e0, const RotSigns& neg, int c, float* y) {
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
+  const qu32x4* src = (const qu32x4*)((const unsigned short*)x + e0);
+  double v[32];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const qu32x4 w = src[h];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = 8 * h + 2 * k;
+      const uint32_t p = w[k] ^ neg.w[t / 2];
+      v[t] = (double)q_u2f(p << 16);
+      v[t + 1] = (double)q_u2f(p & 0xffff0000u);
+    }
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-    if (signs[8 * c + t] < 0) v[t] = -v[t];
+  for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 32; ++t)
       if ((t & h) == 0) {
         const double a = v[t], b = v[t + h];
         v[t] = a + b;
         v[t + h] = a - b;
       }
+  // the lane with the higher element index keeps lower - upper
+  {
+    const double w1 = (c & 1) ? -1.0 : 1.0;
 #pragma unroll
-  for (int m = 1; m < D / 8; m <<= 1) {
-    const bool upper = (c & m) != 0;
+    for (int t = 0; t < 32; ++t) v[t] = __builtin_fma(v[t], w1, quad_xor<1>(v[t]));
+  }
+  if constexpr (D == 128) {
+    const double w2 = (c & 2) ? -1.0 : 1.0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const double other = __shfl_xor(v[t], m);
-      v[t] = upper ? other - v[t] : v[t] + other;
-    }
+    for (int t = 0; t < 32; ++t) v[t] = __builtin_fma(v[t], w2, quad_xor<2>(v[t]));
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t) y[t] = (float)v[t];
+  for (int t = 0; t < 32; ++t) y[t] = (float)v[t];
 }
 
-// grid = (blocks per head, B*H); rows of D bf16, D/8 lanes per row
+// grid = (blocks per head, B*H); rows of D bf16, D/32 lanes per row
 template <int D>
 __global__ void __launch_bounds__(256) fa_rot_amax_kernel(const void* x, const signed char* signs,
                                                           uint32_t* amax_bits, int N) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  constexpr int TPR = D / 32, RPB = 256 / TPR;
   const int bh = blockIdx.y;
   const int c = threadIdx.x % TPR;
+  const RotSigns neg = rot_sign_mask(signs, c);
   float m = 0.0f;
-  // every lane runs the same trip count so that the row's shuffles stay whole
   for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
     const int r = r0 + threadIdx.x / TPR;
     const int rr = r < N ? r : N - 1;          // a row past the end repeats the last one
-    float y[8];
-    rotate_row8<D>(x, ((size_t)bh * N + rr) * D + 8 * c, signs, c, y);
+    float y[32];
+    rotate_row32<D>(x, ((size_t)bh * N + rr) * D + 32 * c, neg, c, y);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(y[t]));
+    for (int t = 0; t < 32; ++t) m = fmaxf(m, fabsf(y[t]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -189,28 +224,33 @@ __global__ void __launch_bounds__(256) fa_rot_amax_kernel(const void* x, const s
 template <int D>
 __global__ void __launch_bounds__(256) fa_rot_quant_kernel(const void* x, const signed char* signs,
                                                            uint8_t* out, const uint32_t* amax_bits, int N) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  constexpr int TPR = D / 32, RPB = 256 / TPR;
   const int bh = blockIdx.y;
   const int c = threadIdx.x % TPR;
+  const RotSigns neg = rot_sign_mask(signs, c);
   const float amax = q_u2f(amax_bits[bh]);
   const float mult = amax == 0.0f ? 1.0f : 448.0f / amax;
   for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
     const int r = r0 + threadIdx.x / TPR;
     const int rr = r < N ? r : N - 1;
-    float y[8];
-    rotate_row8<D>(x, ((size_t)bh * N + rr) * D + 8 * c, signs, c, y);
-    uint2 o;
-    int pk0 = 0, pk1 = 0;
-    float z[8];
+    float y[32];
+    rotate_row32<D>(x, ((size_t)bh * N + rr) * D + 32 * c, neg, c, y);
+    qu32x4 o[2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) z[t] = fminf(fmaxf(y[t] * mult, -448.0f), 448.0f);
-    pk0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], pk0, false);
-    pk0 = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pk0, true);
-    pk1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[4], z[5], pk1, false);
-    pk1 = __builtin_amdgcn_cvt_pk_fp8_f32(z[6], z[7], pk1, true);
-    o.x = (uint32_t)pk0;
-    o.y = (uint32_t)pk1;
-    if (r < N) *(uint2*)(out + ((size_t)bh * N + r) * D + 8 * c) = o;
+    for (int w = 0; w < 8; ++w) {
+      float z[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) z[t] = fminf(fmaxf(y[4 * w + t] * mult, -448.0f), 448.0f);
+      int pk = 0;
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], pk, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pk, true);
+      o[w >> 2][w & 3] = (uint32_t)pk;
+    }
+    if (r < N) {
+      qu32x4* dst = (qu32x4*)(out + ((size_t)bh * N + r) * D + 32 * c);
+      dst[0] = o[0];
+      dst[1] = o[1];
+    }
   }
 }
 
@@ -296,30 +336,32 @@ template <int D>
 __global__ void __launch_bounds__(256) fa_mx_rows_rot_kernel(const void* x, const signed char* signs,
                                                              uint8_t* out, uint8_t* scales, int N,
                                                              float post) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  constexpr int TPR = D / 32, RPB = 256 / TPR;
   const int bh = blockIdx.y;
   const int c = threadIdx.x % TPR;
+  const RotSigns neg = rot_sign_mask(signs, c);
   for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
     const int r = r0 + threadIdx.x / TPR;
     const int rr = r < N ? r : N - 1;   // a row past the end repeats the last one
-    float y[8];
-    rotate_row8<D>(x, ((size_t)bh * N + rr) * D + 8 * c, signs, c, y);
+    float y[32];
+    rotate_row32<D>(x, ((size_t)bh * N + rr) * D + 32 * c, neg, c, y);
+    // the lane's 32 values are exactly one block
     float m = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 32; ++t) {
       y[t] *= post;
       m = fmaxf(m, fabsf(y[t]));
     }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
     const int e = mx_block_exp(m);
     const float mult = mx_exp2i(-e);
-    uint2 o;
-    o.x = mx_pack4(y, mult);
-    o.y = mx_pack4(y + 4, mult);
+    qu32x4 o[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) o[w >> 2][w & 3] = mx_pack4(y + 4 * w, mult);
     if (r < N) {
-      *(uint2*)(out + ((size_t)bh * N + r) * D + 8 * c) = o;
-      if ((c & 3) == 0) scales[((size_t)bh * N + r) * (D / 32) + c / 4] = (uint8_t)(e + 127);
+      qu32x4* dst = (qu32x4*)(out + ((size_t)bh * N + r) * D + 32 * c);
+      dst[0] = o[0];
+      dst[1] = o[1];
+      scales[((size_t)bh * N + r) * (D / 32) + c] = (uint8_t)(e + 127);
     }
   }
 }
