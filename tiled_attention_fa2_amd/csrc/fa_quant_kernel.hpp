@@ -367,8 +367,10 @@ __global__ void __launch_bounds__(256) fa_mx_rows_rot_kernel(const void* x, cons
 }
 
 // Key blocks (V): thread t takes 4 consecutive columns of one 32-key block of
-// one head: items = B*H * ceil(N/32) * D/4; two passes over the block's rows
-// (amax, then codes), one dword of codes per key and one of scale bytes.
+// one head: items = B*H * ceil(N/32) * D/4; one dword of codes per key and one
+// of scale bytes. A whole bf16 block is read once into registers (amax, then
+// codes from the registers); fp32 input and a ragged last block take two
+// passes over the block's rows.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) fa_mx_keys_kernel(const void* x, uint8_t* out, uint8_t* scales,
                                                          int N, int nkb, long long items) {
@@ -394,27 +396,62 @@ __global__ void __launch_bounds__(256) fa_mx_keys_kernel(const void* x, uint8_t*
       for (int i = 0; i < 4; ++i) v[i] = q_u2f(w[i]);
     }
   };
-  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k = k0; k < k1; ++k) {
-    float v[4];
-    load4(k, v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
-  }
-  int e[4];
-  float mult[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    e[i] = mx_block_exp(m[i]);
-    mult[i] = mx_exp2i(-e[i]);
-  }
-  for (int k = k0; k < k1; ++k) {
-    float v[4];
-    load4(k, v);
+  auto store4 = [&](int k, const float* v, const float* mult) {
     int pk = 0;
     pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * mult[0], v[1] * mult[1], pk, false);
     pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * mult[2], v[3] * mult[3], pk, true);
     *(uint32_t*)(out + ((size_t)bh * N + k) * D + 4 * cg) = (uint32_t)pk;
+  };
+  float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int e[4];
+  float mult[4];
+  if (BF16 && k1 - k0 == 32) {
+    // the block's raw bf16 pairs stay in registers (64 of them)
+    uint2 w[32];
+    auto unpack = [](uint2 p, float* v) {
+      v[0] = q_u2f(p.x << 16);
+      v[1] = q_u2f(p.x & 0xffff0000u);
+      v[2] = q_u2f(p.y << 16);
+      v[3] = q_u2f(p.y & 0xffff0000u);
+    };
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      w[k] = *(const uint2*)((const unsigned short*)x + ((size_t)bh * N + k0 + k) * D + 4 * cg);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      float v[4];
+      unpack(w[k], v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[i] = mx_block_exp(m[i]);
+      mult[i] = mx_exp2i(-e[i]);
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      float v[4];
+      unpack(w[k], v);
+      store4(k0 + k, v, mult);
+    }
+  } else {
+    for (int k = k0; k < k1; ++k) {
+      float v[4];
+      load4(k, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[i] = mx_block_exp(m[i]);
+      mult[i] = mx_exp2i(-e[i]);
+    }
+    for (int k = k0; k < k1; ++k) {
+      float v[4];
+      load4(k, v);
+      store4(k, v, mult);
+    }
   }
   const uint32_t sc = (uint32_t)(e[0] + 127) | ((uint32_t)(e[1] + 127) << 8) |
                       ((uint32_t)(e[2] + 127) << 16) | ((uint32_t)(e[3] + 127) << 24);
