@@ -36,12 +36,15 @@ extern "C" int fa_quantize_fp8(const void* x, int in_dtype, void* x_fp8, float* 
     if (bph < 1) bph = 1;
     if (bph > 256) bph = 256;
     const dim3 grid((unsigned)bph, (unsigned)nbh);
+    // the amax pass reads only: a quarter of the workgroups, each streaming
+    // four times as much (measured 131 -> 100 us on a 56 x 30272 x 128 tensor)
+    const dim3 grid_a((unsigned)((bph + 3) / 4), (unsigned)nbh);
     if (in_dtype == FA_DTYPE_BF16) {
-      hipLaunchKernelGGL(fa::fa_amax_kernel<true>, grid, dim3(256), 0, stream, x, amax, per_head);
+      hipLaunchKernelGGL(fa::fa_amax_kernel<true>, grid_a, dim3(256), 0, stream, x, amax, per_head);
       hipLaunchKernelGGL(fa::fa_quant_kernel<true>, grid, dim3(256), 0, stream, x,
                          (uint8_t*)x_fp8, (const uint32_t*)amax, per_head);
     } else {
-      hipLaunchKernelGGL(fa::fa_amax_kernel<false>, grid, dim3(256), 0, stream, x, amax, per_head);
+      hipLaunchKernelGGL(fa::fa_amax_kernel<false>, grid_a, dim3(256), 0, stream, x, amax, per_head);
       hipLaunchKernelGGL(fa::fa_quant_kernel<false>, grid, dim3(256), 0, stream, x,
                          (uint8_t*)x_fp8, (const uint32_t*)amax, per_head);
     }

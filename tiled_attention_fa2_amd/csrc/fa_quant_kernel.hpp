@@ -62,14 +62,29 @@ __global__ void __launch_bounds__(256) fa_amax_kernel(const void* x, uint32_t* a
   const int bh = blockIdx.y;
   const size_t head0 = (size_t)bh * (size_t)per_head;
   const long long n16 = per_head / 16;
-  float m = 0.0f;
-  for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < n16;
-       t += (long long)gridDim.x * blockDim.x) {
-    float v[16];
-    load16<BF16>(x, head0 + (size_t)t * 16, v);
+  // four strides per trip: every load of the trip is in flight before the
+  // first max, and four independent max chains
+  constexpr int U = 4;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  float mu[U] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x; t0 < n16; t0 += U * stride) {
+    float v[U][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int u = 0; u < U; ++u) {
+      const long long t = t0 + u * stride;
+      if (t < n16) {
+        load16<BF16>(x, head0 + (size_t)t * 16, v[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mu[u] = fmaxf(mu[u], fabsf(v[u][i]));
   }
+  float m = fmaxf(fmaxf(mu[0], mu[1]), fmaxf(mu[2], mu[3]));
   // wave reduction, then one value per wave through LDS
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
