@@ -4,7 +4,10 @@
 // bits, so the rate reachable on real data sits below the published peak; this
 // measures how far. The loop has the shape of one key tile of the attention
 // kernel's products: a chain of MFMAs on one accumulator (the scores), then
-// MFMAs into four others (the output), with nothing else in between.
+// MFMAs into four others (the output), with nothing else in between. A second
+// kernel runs the same random-data flop stream on the 16x16 MFMA shapes beside
+// the 32x32 ones, with and without exp/fma work interleaved, to show which
+// shape an attention kernel (whose softmax shares the issue slots) should use.
 //
 // Every launch: `blocks` workgroups of 256 threads (4 waves), three waves per
 // SIMD; thread t of workgroup b writes one float to out[256 b + t], nothing
@@ -12,7 +15,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -118,16 +124,102 @@ ceiling_fp8(float* out, int iters) {
   out[tid] = r;
 }
 
+// The same flop stream on the 32x32 and on the 16x16 MFMA shapes, optionally
+// with softmax-like VALU work (an exp2 of an fma, on eight independent chains)
+// issued between the MFMAs at a fixed number per flop. Per wave and iteration:
+// bf16 8 x 32x32x16 or 16 x 16x16x32 (262144 flop), fp8 8 x 32x32x64 or
+// 16 x 16x16x128 (1048576 flop); VALU pairs: 4 (bf16) or 8 (fp8) per 32x32
+// MFMA, half that per 16x16 MFMA, when VALU is set.
+template <bool FP8, bool SHAPE16, bool VALU>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+shape_mix(float* out, int iters) {
+  const uint32_t tid = blockIdx.x * 256u + threadIdx.x;
+  constexpr int NV = VALU ? (FP8 ? 8 : 4) : 0;
+  float x[8];
+  for (int i = 0; i < 8; ++i) x[i] = normalish(tid * 7u + i) * 0.01f;
+  float r = 0.0f;
+  typedef typename std::conditional<FP8, i32x8, bf16x8>::type opnd;
+  // four fp8 operand pairs (8 VGPRs each) keep the wave within the 168 VGPRs of
+  // three waves per SIMD; eight bf16 pairs (4 each) do too
+  constexpr int NQ = FP8 ? 4 : 8;
+  opnd a[NQ], b[NQ];
+  for (int q = 0; q < NQ; ++q)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = tid * 131u + 8u * q + i;
+      if constexpr (FP8) {
+        a[q][i] = fp8x4(h);
+        b[q][i] = fp8x4(h ^ 0x9e3779b9u);
+      } else {
+        a[q][i] = (__bf16)normalish(h);
+        b[q][i] = (__bf16)normalish(h ^ 0x9e3779b9u);
+      }
+    }
+  if constexpr (!SHAPE16) {
+    f32x16 o[4];
+    for (int m = 0; m < 4; ++m) o[m] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(a[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if constexpr (FP8)
+          o[q & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[q % NQ], b[q % NQ], o[q & 3], 0, 0, 0, 127, 0, 127);
+        else
+          o[q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q % NQ], b[q % NQ], o[q & 3], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x[v & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[v & 7], 0.999f, -0.001f));
+      }
+    }
+    for (int m = 0; m < 4; ++m)
+      for (int i = 0; i < 16; ++i) r += o[m][i];
+  } else {
+    f32x4 o[8];
+    for (int m = 0; m < 8; ++m) o[m] = f32x4{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(a[q]));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if constexpr (FP8) {
+          o[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[q % NQ], b[q % NQ], o[q], 0, 0, 0, 127, 0, 127);
+          o[(q + 4) & 7] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[q % NQ], a[q % NQ], o[(q + 4) & 7], 0, 0, 0, 127, 0, 127);
+        } else {
+          o[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q % NQ], b[q % NQ], o[q], 0, 0, 0);
+          o[(q + 4) & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[q % NQ], a[q % NQ], o[(q + 4) & 7], 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x[v & 7] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[v & 7], 0.999f, -0.001f));
+      }
+    }
+    for (int m = 0; m < 8; ++m)
+      for (int i = 0; i < 4; ++i) r += o[m][i];
+  }
+  for (int i = 0; i < 8; ++i) r += x[i];
+  out[tid] = r;
+}
+
 // kind 0 = bf16 (16 MFMAs of 32768 flop per wave per iteration), 1 = fp8
-// (8 MFMAs of 131072 flop). Times `reps` launches after one warm-up launch and
+// (8 MFMAs of 131072 flop); kinds 2..9 = shape_mix with 2 + 4 fp8 + 2 shape16
+// + valu (random operands whatever `random` says). Times `reps` launches after one warm-up launch and
 // returns the mean milliseconds per launch in *ms; 0 on success, -1 on a HIP
 // error.
 extern "C" int mfma_ceiling_run(int kind, int random, int blocks, int iters, int reps, float* ms) {
-  if (blocks < 1 || iters < 1 || reps < 1 || !ms) return -1;
+  if (kind < 0 || kind > 9 || blocks < 1 || iters < 1 || reps < 1 || !ms) return -1;
   float* out = nullptr;
   if (hipMalloc(&out, (size_t)blocks * 256 * sizeof(float)) != hipSuccess) return -1;
   auto launch = [&]() {
     const dim3 g((unsigned)blocks), b(256);
+    switch (kind) {
+      case 2: hipLaunchKernelGGL((shape_mix<false, false, false>), g, b, 0, 0, out, iters); return;
+      case 3: hipLaunchKernelGGL((shape_mix<false, false, true>), g, b, 0, 0, out, iters); return;
+      case 4: hipLaunchKernelGGL((shape_mix<false, true, false>), g, b, 0, 0, out, iters); return;
+      case 5: hipLaunchKernelGGL((shape_mix<false, true, true>), g, b, 0, 0, out, iters); return;
+      case 6: hipLaunchKernelGGL((shape_mix<true, false, false>), g, b, 0, 0, out, iters); return;
+      case 7: hipLaunchKernelGGL((shape_mix<true, false, true>), g, b, 0, 0, out, iters); return;
+      case 8: hipLaunchKernelGGL((shape_mix<true, true, false>), g, b, 0, 0, out, iters); return;
+      case 9: hipLaunchKernelGGL((shape_mix<true, true, true>), g, b, 0, 0, out, iters); return;
+      default: break;
+    }
     if (kind == 0) {
       if (random) hipLaunchKernelGGL(ceiling_bf16<true>, g, b, 0, 0, out, iters);
       else hipLaunchKernelGGL(ceiling_bf16<false>, g, b, 0, 0, out, iters);

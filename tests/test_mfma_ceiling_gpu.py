@@ -8,6 +8,12 @@ clock to drop, so the rate real attention inputs can reach is lower. This
 prints both rates (the figures the design notes quote) and checks only what
 must hold on any device: both run, and random data is never faster than
 constant data by more than the timing noise.
+
+The second test runs one random-data flop stream on the 32x32 and on the
+16x16 MFMA shapes, alone and with exp2/fma work between the MFMAs at a fixed
+ratio to the flops (as a softmax adds it). It prints the four rates per dtype
+and checks only that every variant runs: which shape wins is a property of the
+device, quoted in the design notes, not something a test can fix.
 """
 import ctypes
 import os
@@ -39,3 +45,21 @@ def test_sustained_mfma_rate(kind, name, iters):
           f"random operands {rand:.0f} TFLOP/s ({100 * rand / PEAK[kind]:.1f}% of peak)", flush=True)
     assert const > 0 and rand > 0
     assert rand <= 1.05 * const
+
+
+def test_mfma_shapes_with_and_without_valu():
+    assert torch.cuda.is_available()
+    lib = ctypes.CDLL(LIB)
+    lib.mfma_ceiling_run.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_float)]
+    blocks, iters = 768, 20000
+    for fp8, name, flop in ((0, "bf16", 8 * 32768.0), (1, "fp8", 8 * 131072.0)):
+        for valu in (0, 1):
+            rates = []
+            for shape16 in (0, 1):
+                kind = 2 + 4 * fp8 + 2 * shape16 + valu
+                ms = ctypes.c_float(0.0)
+                assert lib.mfma_ceiling_run(kind, 1, blocks, iters, 2, ctypes.byref(ms)) == 0
+                rates.append(blocks * 4 * iters * flop / (ms.value * 1e-3) / 1e12)
+            print(f"{name} {'with' if valu else 'without'} exp/fma work: 32x32 {rates[0]:.0f} TFLOP/s, "
+                  f"16x16 {rates[1]:.0f} TFLOP/s", flush=True)
+            assert min(rates) > 0
