@@ -72,7 +72,10 @@ typedef enum {
  *            the scaled scores of each query row (for FP8: of the dequantised
  *            scores), L_i = log sum_j exp(S_ij).
  *   B, H, N  batch, heads, sequence length (queries = keys = N). N == 0 or
- *            B*H == 0 returns FA_OK without launching.
+ *            B*H == 0 returns FA_OK without launching. One head is
+ *            addressed with 32-bit byte offsets: (N + 128) * d * (bytes per
+ *            element) above INT_MAX returns FA_ERR_SHAPE (bf16, d = 128:
+ *            N <= 8388479), as does B*H*ceil(N/128) above INT_MAX.
  *   d        head dimension, 64 or 128.
  *   causal   non-zero: key j is seen by query i only if j <= i.
  *   scale    multiplies Q K^T; any finite value (callers pass 1/sqrt(d)).

@@ -88,6 +88,11 @@ def _fwd(lib, q=A, k=A, v=A, o=A2, lse=A2, B=1, H=1, N=128, d=128, causal=0, sca
     (dict(q=MIS), -7), (dict(v=MIS), -7), (dict(o=MIS), -7),
     (dict(N=0), 0), (dict(B=0), 0), (dict(H=0), 0),
     (dict(B=1 << 20, H=1 << 12, N=4096), -2),
+    # one head is addressed with 32-bit byte offsets: (N + 128) * d * bytes per
+    # element must not exceed INT_MAX (a tile may read up to 128 rows past N)
+    (dict(N=(1 << 31) // 256 - 128), -2),                           # bf16, d = 128: 2^31 bytes
+    (dict(N=(1 << 31) // 128 - 128, dtype=2, descales=A2), -2),     # fp8, d = 128
+    (dict(N=(1 << 31) // 256 - 128, d=64, dtype=0), -2),            # fp32, d = 64
 ])
 def test_fwd_validation_codes(lib, kw, code):
     assert _fwd(lib, **kw) == code
