@@ -95,6 +95,29 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def make_qkv_long(N: int, d: int, seed: int = 0, chunk_rows: int = 1 << 18, threads: int = 16):
+    """One head (B = H = 1) of bf16 Q, K, V for sequences too long for one
+    sequential generator: rows [c*chunk_rows, (c+1)*chunk_rows) of tensor t
+    (0 = Q, 1 = K, 2 = V) are iid N(0,1) float32 from a generator seeded with
+    (seed * 3 + t) * 2^20 + c, rounded to bf16. Chunks are drawn on a thread
+    pool; the result depends only on (N, d, seed, chunk_rows)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    assert N >= 0 and chunk_rows > 0
+    out = [torch.empty((1, 1, N, d), dtype=torch.bfloat16) for _ in range(3)]
+    n_chunks = (N + chunk_rows - 1) // chunk_rows
+
+    def draw(job):
+        t, c = job
+        g = torch.Generator().manual_seed((seed * 3 + t) * (1 << 20) + c)
+        r0, r1 = c * chunk_rows, min(N, (c + 1) * chunk_rows)
+        out[t][0, 0, r0:r1] = torch.randn((r1 - r0, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        list(pool.map(draw, [(t, c) for t in range(3) for c in range(n_chunks)]))
+    return tuple(out)
+
+
 def make_gqa(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0):
     """Q with Hq heads, then K and V with Hkv heads: iid N(0,1) float32 from one
     seeded generator in that order, rounded to bf16 unless dtype == "f32"."""
