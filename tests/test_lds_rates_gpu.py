@@ -10,9 +10,10 @@ Patterns (32-row tiles of 256-byte bf16 rows, 16-byte chunks XOR-swizzled):
   * contiguous baselines.
 Checked (printed in full): the swizzled row-major read runs at the speed of
 a contiguous one; a transposed read of 512 bytes costs a wave at least as
-long as a 1 KB row-major read, i.e. twice as long per byte; and one wave
-alone sees the same per-read time as one wave on each of the four SIMDs, so
-the limit is each SIMD's read rate rather than the shared LDS.
+long as a 1 KB row-major read, i.e. twice as long per byte; and, for the two
+patterns the kernels use, one wave alone sees the same per-read time as one
+wave on each of the four SIMDs, so the limit is each SIMD's read rate rather
+than the shared LDS. Each rate is the fastest of three runs.
 """
 import ctypes
 import os
@@ -41,14 +42,20 @@ def _tr(swz, t=0, n=0):
     return out
 
 
-def _run(lib, kind, offs, waves, trips=2000):
+def _run(lib, kind, offs, waves, trips=2000, repeats=3):
+    """Cycles per read per wave: the fastest of `repeats` runs (anything else
+    on the CU only ever slows a run down)."""
     assert len(offs) == 64 and all(0 <= o and o + 15 * 2048 + 16 <= 65536 for o in offs)
     assert all(o % (16 if kind == 0 else 8) == 0 for o in offs)
     o = torch.tensor(offs, dtype=torch.int32, device="cuda")
     sink = torch.zeros(64 * waves, dtype=torch.int32, device="cuda")
     cyc = torch.zeros(1, dtype=torch.int64, device="cuda")
-    assert lib.lds_rate_run(kind, o.data_ptr(), sink.data_ptr(), cyc.data_ptr(), trips, 64 * waves) == 0
-    return cyc.item() / (trips * 16)
+    best = None
+    for _ in range(repeats):
+        assert lib.lds_rate_run(kind, o.data_ptr(), sink.data_ptr(), cyc.data_ptr(), trips, 64 * waves) == 0
+        c = cyc.item() / (trips * 16)
+        best = c if best is None else min(best, c)
+    return best
 
 
 def test_lds_read_rates():
@@ -68,5 +75,6 @@ def test_lds_read_rates():
               f"{waves * nbytes / c:6.1f} B/cycle for the CU", flush=True)
     assert res[("b128 rows, swizzle row&7", 1)] <= 1.10 * res[("b128 contiguous", 1)]
     assert res[("tr16 rows, swizzle row&7", 1)] >= 1.0 * res[("b128 contiguous", 1)]
-    for name in ("b128 contiguous", "tr16 rows, swizzle row&7"):
+    # the per-SIMD claim, on the two patterns the kernels read with
+    for name in ("b128 rows, swizzle row&7", "tr16 rows, swizzle row&7"):
         assert res[(name, 4)] <= 1.25 * res[(name, 1)]
