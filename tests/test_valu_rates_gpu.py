@@ -6,7 +6,7 @@ function unit does the rest). Two waves share each SIMD; the test prints the
 time of each pairing and checks only what the design relies on: an FMA
 polynomial exp2 costs more than v_exp_f32, and v_exp_f32 next to an FMA wave
 does not run as if on a separate unit (the pair takes clearly longer than
-the exp wave alone).
+the exp wave alone). Each time is the fastest of three launches.
 """
 import ctypes
 import os
@@ -27,9 +27,12 @@ def test_valu_issue_costs():
     t = {}
     for pair, name in ((10, "fma"), (20, "exp"), (30, "poly exp2"), (11, "fma+fma"), (22, "exp+exp"),
                        (12, "fma+exp"), (23, "exp+poly")):
-        us = ctypes.c_float(0.0)
-        assert lib.valu_pair_run(pair, 1000, ctypes.byref(us)) == 0
-        t[name] = us.value
+        runs = []
+        for _ in range(3):          # the fastest of three: noise only slows a run
+            us = ctypes.c_float(0.0)
+            assert lib.valu_pair_run(pair, 1000, ctypes.byref(us)) == 0
+            runs.append(us.value)
+        t[name] = min(runs)
     err = ctypes.c_float(0.0)
     assert lib.poly_exp2_error(ctypes.byref(err)) == 0
     print("us per launch: " + ", ".join(f"{k} {v:.0f}" for k, v in t.items()), flush=True)
