@@ -235,11 +235,11 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
 
 /*
  * fa_splitkv_default_splits -- the num_splits this library picks for a shape
- * on the current device: 1 when the B*H*ceil(N/128) workgroups of fa_fwd
- * already fill every compute unit as many times as it holds workgroups at once
- * (three for head dim 128 in bf16 / FP8, two otherwise); else the number of
- * chunks that does, at most one chunk per 256 keys and at most 16. Always
- * returns a value >= 1 (1 for invalid arguments or a failed device query).
+ * on the current device, with C compute units and W = B*H*ceil(N/128)
+ * workgroups of fa_fwd: 1 when W >= 2C; else ceil(2C / W) (non-causal) or
+ * ceil(3C / W) (causal), at most N / 1024 (no chunk under 1024 keys) and at
+ * most 16. Always returns a value >= 1 (1 for invalid arguments or a failed
+ * device query).
  */
 int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype);
 

@@ -267,20 +267,12 @@ extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num
 }
 
 extern "C" int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype) {
-  (void)causal;
+  (void)dtype;
   if (B <= 0 || H <= 0 || N <= 0) return 1;
   if (d != 64 && d != 128) return 1;
   const int cus = device_cus();
   if (cus <= 0) return 1;
-  const long long resident = (d == 128 && dtype != FA_DTYPE_F32) ? 3 : 2;
-  const long long slots = (long long)cus * resident;
-  const long long wgs = (long long)B * H * ceil_div(N, kBM);
-  if (wgs >= slots) return 1;
-  long long s = ceil_div(slots, wgs);
-  const long long by_keys = N / 256 > 1 ? N / 256 : 1;
-  if (s > by_keys) s = by_keys;
-  if (s > 16) s = 16;
-  return (int)(s < 1 ? 1 : s);
+  return fa_api::default_splits((long long)B * H * ceil_div(N, kBM), N, causal != 0, cus);
 }
 
 extern "C" int fa_merge_partials(const float* o_parts, const float* lse_parts, int num_parts,
