@@ -194,3 +194,38 @@ def test_split_errors_raise():
     with pytest.raises(fa.FAError) as e:
         fa.fwd(*dev, num_splits=fa.FA_MAX_SPLITS + 1)
     assert e.value.status == -10
+
+
+def test_caller_workspace_is_checked_on_every_path():
+    """A caller's workspace reaches the library with its own size, so one that
+    is too small is refused (FA_ERR_WORKSPACE, before any launch) on the
+    split-KV, grouped-query, per-block FP8 and backward paths; one that is not
+    a contiguous uint8 device tensor is refused by the binding."""
+    print("[case] caller workspaces: too small / wrong dtype on fwd, gqa, mxfp8, bwd", flush=True)
+    N, d = 256, 128
+    q, k, v = (t.cuda() for t in make_qkv(1, 2, N, d, "bf16", seed=2))
+    need = fa.splitkv_workspace_bytes(1, 2, N, d, 2)
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    wrong = torch.empty(need // 4 + 16, dtype=torch.float32, device="cuda")
+    k1, v1 = k[:, :1].contiguous(), v[:, :1].contiguous()
+    m8 = fa.quantize_qkv_mxfp8(q, k, v)
+    calls = [
+        ("fwd split", lambda ws: fa.fwd(q, k, v, num_splits=2, workspace=ws)),
+        ("fwd gqa split", lambda ws: fa.fwd(q, k1, v1, num_splits=2, workspace=ws)),
+        ("fwd_mxfp8 split", lambda ws: fa.fwd_mxfp8(*m8[:3], m8[3], num_splits=2, workspace=ws)),
+    ]
+    for name, call in calls:
+        with pytest.raises(fa.FAError) as e:
+            call(small)
+        assert e.value.status == -9, name
+        with pytest.raises(ValueError, match="workspace"):
+            call(wrong)
+    o, lse = fa.fwd(q, k, v, num_splits=1)
+    do = torch.ones_like(q)
+    bneed = fa.bwd_workspace_bytes(1, 2, N)
+    with pytest.raises(fa.FAError) as e:
+        fa.bwd(q, k, v, o, lse, do, workspace=torch.empty(bneed - 16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == -9
+    with pytest.raises(ValueError, match="workspace"):
+        fa.bwd(q, k, v, o, lse, do, workspace=torch.empty(bneed, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()

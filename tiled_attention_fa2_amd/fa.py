@@ -108,6 +108,16 @@ def _call(name: str, dev: torch.device, *args) -> int:
         return getattr(lib(), name)(*args, torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _check_workspace(ws) -> int:
+    """Size in bytes of a caller's workspace (0 for None); it must be a
+    contiguous uint8 device tensor, so that numel() is its size in bytes."""
+    if ws is None:
+        return 0
+    if ws.dtype != torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    return ws.numel()
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DTYPE_F32
@@ -194,10 +204,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
         need = splitkv_workspace_bytes(B, H, N, d, num_splits) if num_splits > 1 else 0
         if num_splits > 1 and workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = _check_workspace(workspace)
         dev = _device(q, k, v, out, lse, descales, workspace)
         st = _call("fa_fwd_gqa", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, N, d,
-                   1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace),
-                   0 if workspace is None else workspace.numel())
+                   1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace), ws_bytes)
         if st != FA_OK:
             raise FAError(st, "fa_fwd_gqa")
         return out, lse
@@ -211,12 +221,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
     need = splitkv_workspace_bytes(B, H, N, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    ws_bytes = _check_workspace(workspace)
     dev = _device(q, k, v, out, lse, descales, workspace)
     st = _call("fa_fwd_splitkv", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-               1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace),
-               workspace.numel())
+               1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace), ws_bytes)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
     return out, lse
@@ -414,11 +422,12 @@ def fwd_mxfp8(q, k, v, scales, causal: bool = False, scale: float | None = None,
     if (o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous()
             or tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise ValueError("out must be bf16 [B, Hq, N, d] and lse float32 [B, Hq, N], contiguous")
-    ws_bytes = 0
-    if num_splits > 1:
-        ws_bytes = splitkv_workspace_bytes(B, Hq, N, d, num_splits)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if num_splits > 1 and workspace is None:
+        need = splitkv_workspace_bytes(B, Hq, N, d, num_splits)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    # the caller's workspace is passed with its own size: the library refuses
+    # one that is too small
+    ws_bytes = _check_workspace(workspace) if num_splits > 1 else 0
     dev = _device(q, k, v, qs, ks, vs, o, lse, workspace)
     st = _call("fa_fwd_mxfp8", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(o),
                _ptr(lse), B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), int(num_splits),
@@ -458,10 +467,11 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
             raise ValueError(f"{name} has the wrong dtype, shape or layout")
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace)
     dev = _device(q, k, v, o, do, lse, dq, dk, dv, workspace)
     st = _call("fa_bwd", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                _ptr(dv), B, H, Hkv, N, d, 1 if causal else 0, float(scale), DTYPE_BF16, _ptr(workspace),
-               workspace.numel())
+               ws_bytes)
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
