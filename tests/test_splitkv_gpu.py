@@ -229,3 +229,33 @@ def test_caller_workspace_is_checked_on_every_path():
     with pytest.raises(ValueError, match="workspace"):
         fa.bwd(q, k, v, o, lse, do, workspace=torch.empty(bneed, dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
+
+
+def test_caller_outputs_are_checked():
+    """Outputs a caller passes in must have exactly the dtype and shape the
+    kernels write (contiguous, on the device): a wrong one is refused by the
+    binding before any launch."""
+    print("[case] caller outputs of the wrong dtype / shape", flush=True)
+    x = torch.ones((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    u8_short = torch.empty((1, 2, 63, 128), dtype=torch.uint8, device="cuda")
+    f32_short = torch.empty(1, dtype=torch.float32, device="cuda")
+    signs = torch.ones(128, dtype=torch.int8, device="cuda")
+    bad = [
+        lambda: fa.quantize_fp8(x, out=u8_short),
+        lambda: fa.quantize_fp8(x, descale=f32_short),
+        lambda: fa.quantize_fp8_rotated(x, signs, False, out=u8_short),
+        lambda: fa.quantize_fp8_rotated(x, signs, False, descale=torch.empty(2, dtype=torch.float64, device="cuda")),
+        lambda: fa.quantize_mxfp8_rows(x, scales=torch.empty((1, 2, 64, 2), dtype=torch.uint8, device="cuda")),
+        lambda: fa.quantize_mxfp8_keys(x, scales=torch.empty((1, 2, 64, 128), dtype=torch.uint8, device="cuda")),
+        lambda: fa.merge_partials(torch.zeros((2, 2, 64, 128), device="cuda"), torch.zeros((2, 2, 64), device="cuda"),
+                                  out=torch.empty((2, 64, 128), dtype=torch.float32, device="cuda")),
+        lambda: fa.merge_partials(torch.zeros((2, 2, 64, 128), device="cuda"), torch.zeros((2, 2, 64), device="cuda"),
+                                  lse=torch.empty((2, 63), dtype=torch.float32, device="cuda")),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    o, lse = fa.fwd(x, x, x)
+    with pytest.raises(ValueError, match="dk"):
+        fa.bwd(x, x, x, o, lse, x, dk=torch.empty((1, 2, 64, 128), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()

@@ -118,6 +118,13 @@ def _check_workspace(ws) -> int:
     return ws.numel()
 
 
+def _check_out(t, dtype, shape, name):
+    """A caller-provided output must be a contiguous device tensor of exactly
+    this dtype and shape: the kernels write all of it and nothing else."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} {tuple(shape)} device tensor")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DTYPE_F32
@@ -259,6 +266,8 @@ def merge_partials(o_parts, lse_parts, out_dtype=torch.bfloat16, out=None, lse=N
         out = torch.empty((BH, N, d), dtype=out_dtype, device=o_parts.device)
     if lse is None:
         lse = torch.empty((BH, N), dtype=torch.float32, device=o_parts.device)
+    _check_out(out, out_dtype, (BH, N, d), "out")
+    _check_out(lse, torch.float32, (BH, N), "lse")
     dev = _device(o_parts, lse_parts, out, lse)
     st = _call("fa_merge_partials", dev, _ptr(o_parts), _ptr(lse_parts), S, 1, BH, N, d, code, _ptr(out),
                _ptr(lse))
@@ -284,6 +293,8 @@ def quantize_fp8(x, out=None, descale=None):
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
+    _check_out(out, torch.uint8, x.shape, "out")
+    _check_out(descale, torch.float32, (B * H,), "descale")
     dev = _device(x, out, descale)
     st = _call("fa_quantize_fp8", dev, _ptr(x), code, _ptr(out), _ptr(descale), B, H, N, d)
     if st != FA_OK:
@@ -309,6 +320,8 @@ def quantize_fp8_rotated(x, signs, fold_inverse_d: bool, out=None, descale=None)
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if descale is None:
         descale = torch.empty(B * H, dtype=torch.float32, device=x.device)
+    _check_out(out, torch.uint8, x.shape, "out")
+    _check_out(descale, torch.float32, (B * H,), "descale")
     dev = _device(x, signs, out, descale)
     st = _call("fa_quantize_fp8_rotated", dev, _ptr(x), DTYPE_BF16, _ptr(signs), _ptr(out), _ptr(descale), B,
                H, N, d, 1 if fold_inverse_d else 0)
@@ -362,6 +375,8 @@ def quantize_mxfp8_rows(x, signs=None, fold_inverse_d: bool = False, out=None, s
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, N, max(d // 32, 1)), dtype=torch.uint8, device=x.device)
+    _check_out(out, torch.uint8, x.shape, "out")
+    _check_out(scales, torch.uint8, (B, H, N, max(d // 32, 1)), "scales")
     dev = _device(x, signs, out, scales)
     st = _call("fa_quantize_mxfp8_rows", dev, _ptr(x), code, _ptr(signs), 1 if fold_inverse_d else 0,
                _ptr(out), _ptr(scales), B, H, N, d)
@@ -380,6 +395,8 @@ def quantize_mxfp8_keys(x, out=None, scales=None):
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, (N + 31) // 32, d), dtype=torch.uint8, device=x.device)
+    _check_out(out, torch.uint8, x.shape, "out")
+    _check_out(scales, torch.uint8, (B, H, (N + 31) // 32, d), "scales")
     dev = _device(x, out, scales)
     st = _call("fa_quantize_mxfp8_keys", dev, _ptr(x), code, _ptr(out), _ptr(scales), B, H, N, d)
     if st != FA_OK:
@@ -463,8 +480,7 @@ def bwd(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        if t.dtype != torch.bfloat16 or t.shape != ref.shape or not t.is_contiguous():
-            raise ValueError(f"{name} has the wrong dtype, shape or layout")
+        _check_out(t, torch.bfloat16, ref.shape, name)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, H, N), 16), dtype=torch.uint8, device=q.device)
     ws_bytes = _check_workspace(workspace)
