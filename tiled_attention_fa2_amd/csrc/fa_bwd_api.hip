@@ -66,6 +66,9 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.n_tiles = (int)n_tiles;
   a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * kDkdvKB);
   a.causal_order = fa_api::causal_order(BH, a.group, N, d, 2);
+  // a dK/dV item (one key/value head) streams the Q and dO rows of its
+  // `group` query heads: the same rule with group * d bytes per row
+  a.causal_order_kv = fa_api::causal_order(BH / a.group, 1, N, (long long)d * a.group, 2);
   a.scale = scale;
   const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles)),
       g_dkdv((unsigned)(BH / a.group * a.n_ktiles));

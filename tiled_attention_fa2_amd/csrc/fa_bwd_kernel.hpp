@@ -61,6 +61,7 @@ struct BwdArgs {
   int n_tiles;          // 128-row tiles per head (dQ kernel)
   int n_ktiles;         // key tiles per head of the dK/dV kernel (128 KB keys each)
   int causal_order;     // order of the dQ kernel's causal tiles (work_item)
+  int causal_order_kv;  // order of the dK/dV kernel's causal key blocks (work_item, flipped)
   float scale;
 };
 
@@ -392,7 +393,11 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
 
   const int BHkv = p.BH / p.group;
   int bkv, kt;
-  work_item(blockIdx.x, BHkv * p.n_ktiles, p.n_ktiles, 0, bkv, kt);
+  // causal: key block 0 meets every query tile and the last block the fewest,
+  // so the longest items are the first blocks; work_item hands out its last
+  // tiles first, hence the flip (a bijection either way)
+  work_item(blockIdx.x, BHkv * p.n_ktiles, p.n_ktiles, CAUSAL ? p.causal_order_kv : 0, bkv, kt);
+  if constexpr (CAUSAL) kt = p.n_ktiles - 1 - kt;
   const int N = p.N;
   const int k0 = kt * bwd::kRows * KB;
   const int k0w = k0 + 32 * KB * wave;      // the wave's first key; block b: k0w + 32 b
