@@ -66,6 +66,32 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def measured_mfma(workload: str):
+    """MFMA busy fraction and shader clock of the workload's kernel from the
+    committed rocprofv3 --pmc record (SQ_VALU_MFMA_BUSY_CYCLES, SQ_CYCLES),
+    only if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "fa_fwd_dit_mfma_utilisation.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("workloads", {}).get(workload)
+
+
+def counter_fields(workload: str, traffic, kern_ms: float, unsplit: bool = True) -> dict:
+    """The roofline object's counter-derived fields: HBM GB/s (counted bytes
+    over the live kernel time) and the MFMA busy fraction and clock. The
+    counters describe the unsplit kernel: a split-KV run gets None."""
+    if not unsplit:
+        return {"hbm_gbps": None, "mfma_busy_frac": None, "shader_clock_ghz": None}
+    m = measured_mfma(workload)
+    return {"hbm_gbps": round(traffic / (kern_ms * 1e-3) / 1e9, 1) if traffic else None,
+            "mfma_busy_frac": m["mfma_busy_frac"] if m else None,
+            "shader_clock_ghz": m["shader_clock_ghz"] if m else None}
+
+
 def time_fwd(fa, torch, args_in, kw, steps, warmup, fn=None):
     """Warm up, then time exactly `steps` launches of fn (default fa.fwd).
     Returns (region ms per step, mean kernel ms from per-launch events, wall
@@ -237,7 +263,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic if splits == 1 else None,
-                     "kernel": kernel_name(w, splits), "kernel_ms": round(kern_ms, 4)},
+                     "kernel": kernel_name(w, splits), "kernel_ms": round(kern_ms, 4),
+                     **counter_fields(w.name, traffic, kern_ms, splits == 1)},
     }
 
     if not a.no_fp8 and w.dtype == "bf16" and w.name.startswith("bf16_dit"):
@@ -301,7 +328,8 @@ def main():
                          "frac": round(w8.flops() / (kern8 * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                          "traffic": measured_traffic(w8.name) if splits8 == 1 else None,
                          "kernel": kernel_name(w8, splits8),
-                         "kernel_ms": round(kern8, 4)},
+                         "kernel_ms": round(kern8, 4),
+                         **counter_fields(w8.name, measured_traffic(w8.name), kern8, splits8 == 1)},
         }
 
     if a.bwd and w.dtype == "bf16":

@@ -40,5 +40,12 @@ def test_bench_prints_one_contract_line():
     assert roof["traffic"] is None or roof["traffic"] >= 1.7e9   # at least the algorithmic bytes
     fp8 = out["fp8"]
     assert fp8["roofline"]["peak"] == 5000.0 and 0 < fp8["roofline"]["frac"] < 1
+    # counter-derived fields: null, or HBM GB/s under the 8 TB/s peak and an
+    # MFMA busy fraction with a plausible shader clock
+    for r in (roof, fp8["roofline"]):
+        assert r["hbm_gbps"] is None or 0 < r["hbm_gbps"] < 8000
+        assert (r["hbm_gbps"] is None) == (r["traffic"] is None)
+        assert r["mfma_busy_frac"] is None or 0 < r["mfma_busy_frac"] <= 1
+        assert r["shader_clock_ghz"] is None or 0.5 < r["shader_clock_ghz"] < 3.0
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0

@@ -67,3 +67,20 @@ def test_cpu_baseline_leg_times_the_oracle_on_a_sample():
     assert out["value"] > 0 and out["cores"] >= 1
     assert "query rows" in out["sample"] and w.name in out["sample"]
     assert out["extrapolated_full_problem_s"] > 0
+
+
+def test_counter_fields_follow_the_source_they_were_taken_on(monkeypatch, tmp_path):
+    rec = {"source_sha256": "a" * 64, "workloads": {"bf16_dit_b1_h56_n30272_d128": {
+        "kernel": "k", "mfma_busy_frac": 0.63, "shader_clock_ghz": 1.67, "duration_ms": 23.9}}}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "fa_fwd_dit_mfma_utilisation.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "a" * 64)
+    f = bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0)
+    assert f == {"hbm_gbps": 320.0, "mfma_busy_frac": 0.63, "shader_clock_ghz": 1.67}
+    # no traffic record: no bandwidth; a split run: nothing (the counters are of the unsplit kernel)
+    assert bench.counter_fields("bf16_dit_b1_h56_n30272_d128", None, 25.0)["hbm_gbps"] is None
+    assert set(bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0, False).values()) == {None}
+    assert bench.counter_fields("no_such_workload", None, 1.0)["mfma_busy_frac"] is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "b" * 64)
+    assert bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0)["mfma_busy_frac"] is None
