@@ -27,6 +27,7 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak (bf16 / fp8), H=56 N=30272 d=
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense MFMA
 KERNEL_SOURCES = ["tiled_attention_fa2_amd/csrc/fa_fwd_kernel.hpp",
                   "tiled_attention_fa2_amd/csrc/fa_api_common.hpp",
+                  "tiled_attention_fa2_amd/csrc/fa_api_device.hpp",
                   "tiled_attention_fa2_amd/csrc/fa_api.hip"]
 
 

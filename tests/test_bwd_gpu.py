@@ -138,3 +138,39 @@ def test_backward_full_size_sampled():
             tol = 1e-2 * float(np.max(np.abs(ref))) + _floor(ref)
             print(f"    head {h} {name}: max|err|={err:.3e} tol={tol:.3e} cos={_cos(g, ref):.7f}", flush=True)
             assert err <= tol and _cos(g, ref) >= 0.9999, (h, name)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_blocks_per_wave(d, causal):
+    """The dK/dV kernel runs two 32-key blocks per wave when B*Hkv*ceil(N/256)
+    fills the device's compute units, else one (twice the workgroups). 128
+    heads of 512 tokens take two blocks on a 256-CU device; any one head alone
+    takes one. The gradients of a head must be identical either way (the
+    blocks change which workgroup owns a key, never the arithmetic of its
+    gradient), and sampled heads of the 128-head launch must match the oracle."""
+    B, H, N = 1, 128, 512
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert B * H * -(-N // 256) >= cus, "shape no longer selects two blocks per wave on this device"
+    print(f"[case] key blocks per wave d={d} causal={causal} H={H} N={N} cus={cus}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (t.cuda().contiguous() for t in make_qkv(B, H, N, d, "bf16", seed=61))
+    do = make_dout(B, H, N, d, seed=62).cuda().contiguous()
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale, num_splits=1)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for h in (0, 77, H - 1):
+        one = [t[:, h:h + 1].contiguous() for t in (q, k, v, o, lse, do)]
+        g1 = fa.bwd(*one, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        for name, got, full in zip(("dq", "dk", "dv"), g1, (dq, dk, dv)):
+            assert torch.equal(got, full[:, h:h + 1]), (h, name)
+    for h in (0, H - 1):
+        sl = [t[:, h:h + 1].cpu() for t in (q, k, v, do)]
+        dQ, dK, dV, _ = oracle.attention_backward(*sl, scale, causal=causal, o=o[:, h:h + 1].cpu())
+        for name, got, ref in (("dq", dq, dQ), ("dk", dk, dK), ("dv", dv, dV)):
+            g = got[:, h:h + 1].float().cpu().double().numpy()
+            err = float(np.max(np.abs(g - ref)))
+            tol = 1e-2 * float(np.max(np.abs(ref))) + _floor(ref)
+            print(f"    head {h} {name}: max|err|={err:.3e} tol={tol:.3e} cos={_cos(g, ref):.7f}", flush=True)
+            assert np.all(np.isfinite(g)) and err <= tol and _cos(g, ref) >= 0.9999, (h, name)

@@ -9,6 +9,7 @@
 
 #include "fa.h"
 #include "fa_api_common.hpp"
+#include "fa_api_device.hpp"
 #include "fa_fwd_kernel.hpp"
 #include "fa_merge_kernel.hpp"
 
@@ -150,17 +151,6 @@ int prepare_fwd(const void* q, const void* k, const void* v, void* o, float* lse
 }
 
 // Compute units of the current device, cached per device (0 if the query fails).
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < 64) cached[dev] = cus;
-  return cus;
-}
-
 }  // namespace
 
 extern "C" const char* fa_status_string(int status) {
@@ -270,7 +260,7 @@ extern "C" int fa_splitkv_default_splits(int B, int H, int N, int d, int causal,
   (void)dtype;
   if (B <= 0 || H <= 0 || N <= 0) return 1;
   if (d != 64 && d != 128) return 1;
-  const int cus = device_cus();
+  const int cus = fa_api::device_cus();
   if (cus <= 0) return 1;
   return fa_api::default_splits((long long)B * H * ceil_div(N, kBM), N, causal != 0, cus);
 }

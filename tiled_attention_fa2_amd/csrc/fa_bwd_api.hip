@@ -7,6 +7,7 @@
 
 #include "fa.h"
 #include "fa_api_common.hpp"
+#include "fa_api_device.hpp"
 #include "fa_bwd_kernel.hpp"
 
 using fa_api::aligned16;
@@ -64,7 +65,12 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.N = N;
   a.group = Hq / Hkv;
   a.n_tiles = (int)n_tiles;
-  a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * kDkdvKB);
+  // one key block per wave when two would leave compute units idle: twice the
+  // workgroups, each reading its Q / dO operands for one block (measured:
+  // 8 heads x 4096 tokens, 128 workgroups of two blocks against 256 of one)
+  const int cus = fa_api::device_cus();
+  const bool one_block = kDkdvKB == 2 && cus > 0 && (BH / a.group) * ceil_div(N, fa::bwd::kRows * 2) < cus;
+  a.n_ktiles = (int)ceil_div(N, fa::bwd::kRows * (one_block ? 1 : kDkdvKB));
   a.causal_order = fa_api::causal_order(BH, a.group, N, d, 2);
   // a dK/dV item (one key/value head) streams the Q and dO rows of its
   // `group` query heads: the same rule with group * d bytes per row
@@ -76,19 +82,31 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (d == 128) {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<128>, g_pre, blk, 0, stream, a);
     if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
+      if (one_block)
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, 1, 1>), g_dkdv, blk, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true>), g_dq, blk, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
+      if (one_block)
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, 1, 1>), g_dkdv, blk, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false>), g_dq, blk, 0, stream, a);
     }
   } else {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<64>, g_pre, blk, 0, stream, a);
     if (c) {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
+      if (one_block)
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, 1, 1>), g_dkdv, blk, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true>), g_dq, blk, 0, stream, a);
     } else {
-      hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
+      if (one_block)
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, 1, 1>), g_dkdv, blk, 0, stream, a);
+      else
+        hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
       hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false>), g_dq, blk, 0, stream, a);
     }
   }
