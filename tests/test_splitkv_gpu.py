@@ -259,3 +259,27 @@ def test_caller_outputs_are_checked():
     with pytest.raises(ValueError, match="dk"):
         fa.bwd(x, x, x, o, lse, x, dk=torch.empty((1, 2, 64, 128), dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("H,N,causal,expect", [(4, 4096, False, 4), (8, 4096, False, 2), (32, 1024, False, 1),
+                                               (8, 4096, True, 3)])
+def test_default_split_matches_oracle(H, N, causal, expect):
+    """fwd() with the library's own number of key chunks (fa_splitkv_default_splits
+    on a 256-CU device: about two workgroups per CU, three if causal, no chunk
+    under 1024 keys) against the oracle on sampled rows of every head."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = fa.default_splits(1, H, N, 128, causal, fa.DTYPE_BF16)
+    print(f"[case] default split H={H} N={N} causal={causal}: {S} chunks on {cus} CUs", flush=True)
+    if cus == 256:
+        assert S == expect
+    q, k, v = make_qkv(1, H, N, 128, "bf16", seed=H + N)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(N, tile=128, n_random=16)
+    O_ref, L_ref = oracle.attention(q, k, v, scale=128 ** -0.5, causal=causal, rows=rows)
+    got_o = o.float().cpu().double().numpy()[:, :, rows]
+    got_l = lse.cpu().double().numpy()[:, :, rows]
+    floor = float(np.max(np.abs(torch.from_numpy(O_ref).to(torch.bfloat16).double().numpy() - O_ref)))
+    err_o, err_l = float(np.max(np.abs(got_o - O_ref))), float(np.max(np.abs(got_l - L_ref)))
+    print(f"    max|dO|={err_o:.3e} (tol {1e-2 + floor:.3e}) max|dL|={err_l:.3e}", flush=True)
+    assert err_o <= 1e-2 + floor and err_l <= 1e-3
