@@ -30,7 +30,7 @@ GXX = shutil.which("g++")
 
 # (workgroups = B*H*ceil(N/128), N, causal) -> chunks the rule picks with 256 CUs
 MEASURED = {
-    (256, 4096, 0): 2, (256, 8192, 0): 2, (256, 16384, 0): 2, (256, 2048, 0): 2, (256, 1024, 0): 1,
+    (256, 4096, 0): 2, (256, 8192, 0): 2, (256, 16384, 0): 2, (256, 2048, 0): 1, (256, 1024, 0): 1,
     (384, 4096, 0): 2, (512, 8192, 0): 1, (128, 4096, 0): 4, (640, 4096, 0): 1,
     (256, 4096, 1): 3, (512, 4096, 1): 1, (256, 16384, 1): 3,
 }
@@ -69,6 +69,8 @@ def test_invariants(rule):
             assert s == 1                          # the device is already full
         if s > 1:
             assert n // s >= 1024                  # no chunk under 1024 keys
+            if not c and w >= cus:
+                assert n // s >= 2048              # nor under 2048 on a grid already one deep
             # the fewest chunks that reach two (three if causal) workgroups per CU
             assert (s - 1) * w < (3 if c else 2) * cus
     # degenerate arguments
