@@ -6,7 +6,9 @@ B=1, H=56, N=30272, d=128, non-causal, bf16, with iid N(0,1) synthetic inputs
 in place of the model's activations. The same shape in FP8-e4m3 (per-head
 quantised from the same bf16 draws) is timed next to it.
 
-A step is one fa_fwd over the whole batch with inputs resident in HBM.
+A step is one fa_fwd over the whole batch with inputs resident in HBM; 1 GiB is
+written before each timed launch (outside its event pair) so that neither L2 nor
+the MALL holds them, and the reported time is the median per-launch time.
 FLOP per step = 4*B*H*N^2*d (halved for causal), the pages' accounting.
 Prints ONE JSON line.
 """
@@ -82,21 +84,57 @@ def measured_mfma(workload: str):
 
 
 def counter_fields(workload: str, traffic, kern_ms: float, unsplit: bool = True) -> dict:
-    """The roofline object's counter-derived fields: HBM GB/s (counted bytes
-    over the live kernel time) and the MFMA busy fraction and clock. The
+    """The roofline object's counter-derived fields: fabric GB/s (the counted
+    L2-miss bytes over the live kernel time; FETCH_SIZE and WRITE_SIZE count
+    what the L2 reads from and writes to the fabric, MALL hits included, so
+    this is an upper bound on HBM traffic: no HBM-only counter exists) and the MFMA busy fraction and clock. The
     counters describe the unsplit kernel: a split-KV run gets None."""
     if not unsplit:
-        return {"hbm_gbps": None, "mfma_busy_frac": None, "shader_clock_ghz": None}
+        return {"fabric_gbps": None, "mfma_busy_frac": None, "shader_clock_ghz": None}
     m = measured_mfma(workload)
-    return {"hbm_gbps": round(traffic / (kern_ms * 1e-3) / 1e9, 1) if traffic else None,
+    return {"fabric_gbps": round(traffic / (kern_ms * 1e-3) / 1e9, 1) if traffic else None,
             "mfma_busy_frac": m["mfma_busy_frac"] if m else None,
             "shader_clock_ghz": m["shader_clock_ghz"] if m else None}
 
 
-def time_fwd(fa, torch, args_in, kw, steps, warmup, fn=None):
-    """Warm up, then time exactly `steps` launches of fn (default fa.fwd).
-    Returns (region ms per step, mean kernel ms from per-launch events, wall
-    ms per step)."""
+FLUSH_BYTES = 1 << 30    # more than the L2 (8 x 4 MiB) and the 256 MiB MALL together
+
+
+def make_flush(torch, device):
+    """A 1 GiB buffer; writing it before a timed launch evicts the inputs from
+    L2 and MALL, as the pages' harness does ("FlashAttention-2 from PyTorch to
+    Triton", the harness paragraph: do_bench flushes L2 between runs)."""
+    return torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=device)
+
+
+def timed_launches(torch, launch, steps, flush):
+    """Time exactly `steps` launches, each alone between two HIP events on the
+    current stream, with the flush buffer written before each one (outside
+    the event pair). Returns the per-launch times in ms."""
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def stats(times):
+    """Median (the reported statistic, as do_bench reports), mean, min, max."""
+    t = sorted(times)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return {"median_ms": med, "mean_ms": sum(t) / n, "min_ms": t[0], "max_ms": t[-1]}
+
+
+def time_fwd(fa, torch, args_in, kw, steps, warmup, flush, fn=None):
+    """Warm up, then time exactly `steps` launches of fn (default fa.fwd), the
+    caches flushed before each. Returns the per-launch statistics (ms)."""
     fn = fa.fwd if fn is None else fn
     splits = kw.get("num_splits") or 1
     if splits > 1:   # the split-KV workspace, allocated once outside the timed region
@@ -107,25 +145,13 @@ def time_fwd(fa, torch, args_in, kw, steps, warmup, fn=None):
     kw = dict(kw, out=o, lse=lse)
     for _ in range(warmup):
         fn(*args_in, **kw)
-    stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        fn(*args_in, **kw)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    region_ms = starts[0].elapsed_time(ends[-1]) / steps
-    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return max(region_ms, 1e-9), kern_ms, wall_ms
+    return stats(timed_launches(torch, lambda: fn(*args_in, **kw), steps, flush))
 
 
-def time_bwd(fa, torch, w, qd, kd, vd, steps, warmup):
+def time_bwd(fa, torch, w, qd, kd, vd, steps, warmup, flush):
     """The backward on the workload's own inputs: fwd once for O and L, a
-    seeded dO, then `steps` timed fa_bwd calls (HIP events on the stream)."""
+    seeded dO, then `steps` timed fa_bwd calls (HIP events on the stream,
+    caches flushed before each); returns the median ms."""
     from tiled_attention_fa2_amd.inputs import make_dout
 
     o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, num_splits=1)
@@ -135,15 +161,7 @@ def time_bwd(fa, torch, w, qd, kd, vd, steps, warmup):
     kw = dict(causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
     for _ in range(warmup):
         fa.bwd(qd, kd, vd, o, lse, do, **kw)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        fa.bwd(qd, kd, vd, o, lse, do, **kw)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return stats(timed_launches(torch, lambda: fa.bwd(qd, kd, vd, o, lse, do, **kw), steps, flush))["median_ms"]
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -196,7 +214,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bf16_dit_b1_h56_n30272_d128")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -245,12 +263,14 @@ def main():
         main_in, main_kw = (q8, k8, v8), dict(causal=w.causal, scale=w.scale, descales=ds, num_splits=splits)
     else:
         main_in, main_kw = (qd, kd, vd), dict(causal=w.causal, scale=w.scale, num_splits=splits)
+    flush = make_flush(torch, dev)
     print("[bench] timing main leg", file=sys.stderr, flush=True)
-    ms, kern_ms, wall_ms = time_fwd(fa, torch, main_in, main_kw, a.steps, a.warmup)
+    t_main = time_fwd(fa, torch, main_in, main_kw, a.steps, a.warmup, flush)
+    ms = kern_ms = t_main["median_ms"]
     flops = w.flops()
     value = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    achieved = flops / (kern_ms * 1e-3) / 1e12
+    achieved = value
     traffic = measured_traffic(w.name)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -259,8 +279,10 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.kv_heads, "N": w.N, "d": w.d,
                    "causal": w.causal, "num_splits": splits,
-                   "pct_of_mfma_peak": round(100 * value / peak, 2),
-                   "wall_ms_per_step": round(wall_ms, 4)},
+                   "pct_of_mfma_peak": round(100 * value / peak, 2)},
+        "timing": {"statistic": "median of the per-launch HIP event times; 1 GiB written before each "
+                                "launch, outside the event pair, to flush L2 and MALL",
+                   **{k: round(x, 4) for k, x in t_main.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic if splits == 1 else None,
@@ -274,45 +296,28 @@ def main():
         q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)
         splits8 = a.num_splits if a.num_splits is not None else fa.default_splits(
             w8.B, w8.H, w8.N, w8.d, w8.causal, fa.DTYPE_FP8_E4M3)
-        ms8, kern8, _ = time_fwd(fa, torch, (q8, k8, v8),
-                                 dict(causal=False, scale=w8.scale, descales=ds, num_splits=splits8),
-                                 a.steps, a.warmup)
+        t8 = time_fwd(fa, torch, (q8, k8, v8), dict(causal=False, scale=w8.scale, descales=ds, num_splits=splits8),
+                      a.steps, a.warmup, flush)
+        ms8 = kern8 = t8["median_ms"]
         # per-head quantise of Q, K and V (the FP8 path's first step), timed on its own
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(a.steps):
-            fa.quantize_qkv_fp8(qd, kd, vd)
-        e1.record()
-        torch.cuda.synchronize()
-        qms = e0.elapsed_time(e1) / a.steps
+        qms = stats(timed_launches(torch, lambda: fa.quantize_qkv_fp8(qd, kd, vd), a.steps, flush))["median_ms"]
         # the same with Q and K rotated by a randomised Hadamard transform first
         signs = make_signs(w8.d, seed=0).to(dev)
         fa.quantize_qkv_fp8(qd, kd, vd, signs=signs)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(a.steps):
-            fa.quantize_qkv_fp8(qd, kd, vd, signs=signs)
-        e1.record()
-        torch.cuda.synchronize()
-        rqms = e0.elapsed_time(e1) / a.steps
+        rqms = stats(timed_launches(torch, lambda: fa.quantize_qkv_fp8(qd, kd, vd, signs=signs), a.steps,
+                                    flush))["median_ms"]
         # per-block FP8: row-block quantise of Q and K, key-block quantise of
         # V (one pass each), then the forward with the scales in the MFMAs
         mq8, mk8, mv8, msc = fa.quantize_qkv_mxfp8(qd, kd, vd)
-        msm, mskern, _ = time_fwd(fa, torch, (mq8, mk8, mv8, msc),
-                                  dict(causal=False, scale=w8.scale, num_splits=splits8),
-                                  a.steps, a.warmup, fn=fa.fwd_mxfp8)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(a.steps):
-            fa.quantize_qkv_mxfp8(qd, kd, vd)
-        e1.record()
-        torch.cuda.synchronize()
-        mqms = e0.elapsed_time(e1) / a.steps
+        tm = time_fwd(fa, torch, (mq8, mk8, mv8, msc), dict(causal=False, scale=w8.scale, num_splits=splits8),
+                      a.steps, a.warmup, flush, fn=fa.fwd_mxfp8)
+        msm = mskern = tm["median_ms"]
+        mqms = stats(timed_launches(torch, lambda: fa.quantize_qkv_mxfp8(qd, kd, vd), a.steps, flush))["median_ms"]
         del mq8, mk8, mv8, msc
         v8 = w8.flops() / (ms8 * 1e-3) / 1e12
         out["fp8"] = {
             "workload": w8.name, "value": round(v8, 2), "unit": "TFLOP/s", "ms_per_step": round(ms8, 4),
+            "timing": {k: round(x, 4) for k, x in t8.items()},
             "pct_of_mfma_peak": round(100 * v8 / PEAK_TFLOPS["fp8"], 2),
             "quantize_qkv_ms": round(qms, 4),
             "value_incl_quantize": round(w8.flops() / ((ms8 + qms) * 1e-3) / 1e12, 2),
@@ -335,7 +340,7 @@ def main():
 
     if a.bwd and w.dtype == "bf16":
         print("[bench] timing the backward", file=sys.stderr, flush=True)
-        msb = time_bwd(fa, torch, w, qd, kd, vd, a.steps, a.warmup)
+        msb = time_bwd(fa, torch, w, qd, kd, vd, a.steps, a.warmup, flush)
         fb = 2.5 * flops     # five N x N x d products against the forward's two
         out["bwd"] = {"value": round(fb / (msb * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(msb, 4),
                       "flop_convention": "10*B*H*N^2*d (halved for causal): dV, dP, dS-to-dQ, dS-to-dK and the "

@@ -33,6 +33,10 @@ def test_bench_prints_one_contract_line():
     # value is the FLOP count over the timed region
     flops = 4.0 * 56 * 30272 ** 2 * 128
     assert out["value"] == pytest.approx(flops / (out["ms_per_step"] * 1e-3) / 1e12, rel=1e-3)
+    # the reported time is the median of flushed per-launch times
+    t = out["timing"]
+    assert "median" in t["statistic"] and t["min_ms"] <= t["median_ms"] <= t["max_ms"]
+    assert out["ms_per_step"] == pytest.approx(t["median_ms"], rel=1e-3)
     roof = out["roofline"]
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
@@ -40,11 +44,11 @@ def test_bench_prints_one_contract_line():
     assert roof["traffic"] is None or roof["traffic"] >= 1.7e9   # at least the algorithmic bytes
     fp8 = out["fp8"]
     assert fp8["roofline"]["peak"] == 5000.0 and 0 < fp8["roofline"]["frac"] < 1
-    # counter-derived fields: null, or HBM GB/s under the 8 TB/s peak and an
+    # counter-derived fields: null, or L2-miss (fabric) GB/s under the 8 TB/s peak and an
     # MFMA busy fraction with a plausible shader clock
     for r in (roof, fp8["roofline"]):
-        assert r["hbm_gbps"] is None or 0 < r["hbm_gbps"] < 8000
-        assert (r["hbm_gbps"] is None) == (r["traffic"] is None)
+        assert r["fabric_gbps"] is None or 0 < r["fabric_gbps"] < 8000
+        assert (r["fabric_gbps"] is None) == (r["traffic"] is None)
         assert r["mfma_busy_frac"] is None or 0 < r["mfma_busy_frac"] <= 1
         assert r["shader_clock_ghz"] is None or 0.5 < r["shader_clock_ghz"] < 3.0
     cpu = out["cpu_baseline"]

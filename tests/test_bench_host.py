@@ -77,10 +77,22 @@ def test_counter_fields_follow_the_source_they_were_taken_on(monkeypatch, tmp_pa
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "a" * 64)
     f = bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0)
-    assert f == {"hbm_gbps": 320.0, "mfma_busy_frac": 0.63, "shader_clock_ghz": 1.67}
+    assert f == {"fabric_gbps": 320.0, "mfma_busy_frac": 0.63, "shader_clock_ghz": 1.67}
     # no traffic record: no bandwidth; a split run: nothing (the counters are of the unsplit kernel)
-    assert bench.counter_fields("bf16_dit_b1_h56_n30272_d128", None, 25.0)["hbm_gbps"] is None
+    assert bench.counter_fields("bf16_dit_b1_h56_n30272_d128", None, 25.0)["fabric_gbps"] is None
     assert set(bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0, False).values()) == {None}
     assert bench.counter_fields("no_such_workload", None, 1.0)["mfma_busy_frac"] is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "b" * 64)
     assert bench.counter_fields("bf16_dit_b1_h56_n30272_d128", 8.0e9, 25.0)["mfma_busy_frac"] is None
+
+
+def test_timing_statistic_is_the_median():
+    # the reported time is the median of the per-launch times, as the pages'
+    # harness reports; mean, min and max ride along
+    import bench
+
+    st = bench.stats([3.0, 1.0, 2.0])
+    assert st == {"median_ms": 2.0, "mean_ms": 2.0, "min_ms": 1.0, "max_ms": 3.0}
+    assert bench.stats([4.0, 1.0, 2.0, 3.0])["median_ms"] == 2.5
+    assert bench.stats([5.0, 1.0, 1.0, 1.0, 9.0])["median_ms"] == 1.0
+    assert bench.FLUSH_BYTES >= 512 << 20

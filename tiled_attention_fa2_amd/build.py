@@ -29,12 +29,8 @@ FLAGS = [
 
 PROBE_SRC = os.path.join(ROOT, "tests", "hip", "mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_probe.so")
-CEILING_SRC = os.path.join(ROOT, "tests", "hip", "mfma_ceiling.hip")
-CEILING_LIB = os.path.join(ROOT, "tests", "hip", "libmfma_ceiling.so")
-VALU_SRC = os.path.join(ROOT, "tests", "hip", "valu_rates.hip")
-VALU_LIB = os.path.join(ROOT, "tests", "hip", "libvalu_rates.so")
-LDS_SRC = os.path.join(ROOT, "tests", "hip", "lds_rates.hip")
-LDS_LIB = os.path.join(ROOT, "tests", "hip", "liblds_rates.so")
+VARIANTS_SRC = os.path.join(ROOT, "tests", "hip", "stage_variants.hip")
+VARIANTS_LIB = os.path.join(ROOT, "tests", "hip", "libstage_variants.so")
 
 
 def _hipcc(cmd, verbose):
@@ -47,15 +43,14 @@ def _hipcc(cmd, verbose):
 
 
 def build_probe(verbose: bool = False) -> str:
-    """The test helpers of tests/hip: the one-wave MFMA layout/precision probe,
-    the sustained-MFMA-rate probe and the VALU issue-cost probe used by the GPU
-    tests."""
+    """The test helpers of tests/hip: the one-wave MFMA layout/precision probe
+    and the forward kernel at other pipeline depths (the determinism test),
+    both used by the GPU tests."""
     _hipcc([HIPCC, *FLAGS, PROBE_SRC, "-o", PROBE_LIB + ".tmp"], verbose)
     os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
-    for src, lib in ((CEILING_SRC, CEILING_LIB), (VALU_SRC, VALU_LIB), (LDS_SRC, LDS_LIB)):
-        if os.path.exists(src):
-            _hipcc([HIPCC, *FLAGS, src, "-o", lib + ".tmp"], verbose)
-            os.replace(lib + ".tmp", lib)
+    if os.path.exists(VARIANTS_SRC):
+        _hipcc([HIPCC, *FLAGS, VARIANTS_SRC, "-o", VARIANTS_LIB + ".tmp"], verbose)
+        os.replace(VARIANTS_LIB + ".tmp", VARIANTS_LIB)
     return PROBE_LIB
 
 

@@ -35,8 +35,10 @@ void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
   constexpr int BN = DT == fa::kBF16 ? 32 : 64;
   constexpr int NSTAGE = DT == fa::kBF16 ? 3 : 2;
   constexpr int LOOK = 2, WPE = 3;
+  // FP8: the reference max may lag the running max by 0.75 (log2 units)
+  constexpr int TAUQ = DT == fa::kFP8 ? 3 : 0;
   const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
-  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX>),
+  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX, TAUQ>),
                      dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
 }
 

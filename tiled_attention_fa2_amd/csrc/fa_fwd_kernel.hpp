@@ -828,7 +828,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // NSTAGE - 1 tiles ahead. WPE = waves per SIMD the registers must allow.
 // MX: per-block FP8 (E8M0 scales applied by the MFMAs, see FwdArgs).
 template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2,
-          bool SPLIT = false, bool MX = false>
+          bool SPLIT = false, bool MX = false, int TAUQ = 0>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int D = 128;
@@ -883,12 +883,18 @@ fa_fwd_dma_kernel(FwdArgs p) {
     dv = p.descales[p.BH + p.BH / p.group + bkv];
   }
   constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
-  // The running max is exact for FP8 as well: FA-4's conditional rescale
-  // ("Kernels and Memory in LLM Inference", section "FlashAttention-4") with a
-  // reference allowed to lag by 1 (log2 units, P * 128 to stay below 448) was
-  // measured: the dominant weight of a near one-hot row becomes 128 * 2^delta
-  // instead of exactly 256 and takes e4m3's 2^-4 rounding, 0.10 of error in O
-  // on peaked inputs against a 0.075 bound.
+  // Conditional rescale ("Kernels and Memory in LLM Inference", section
+  // "FlashAttention-4"): the reference max that p, l and O are taken against
+  // moves only when a tile's max exceeds it by more than tau = TAUQ / 4 (log2
+  // units); between moves p <= 2^tau (times the bias) and neither O nor l is
+  // rescaled, and the tile skips the alpha work. l and O always share the
+  // reference, so only the rounding of P changes: with tau > 0 the largest
+  // weight of a row is 2^delta instead of exactly 1. FP8 takes tau = 0.75
+  // (P * 256 * 2^0.75 <= 431 stays below e4m3's 448); bf16 keeps tau = 0, as
+  // the bf16 rounding of a dominant weight would eat most of the 1e-2 margin
+  // of causal rows with a handful of keys.
+  constexpr float kTau = 0.25f * TAUQ;
+  static_assert(TAUQ == 0 || (DT == kFP8 && TAUQ <= 3), "tau > 0: FP8 only, P * 256 * 2^tau below 448");
   // a negative scale is folded into Q (sign flip, exact), so c > 0 below
   const bool neg_scale = c < 0.0f;
   c = fabsf(c);
@@ -1007,8 +1013,14 @@ fa_fwd_dma_kernel(FwdArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.0f;
-  float m_run = -__builtin_inff();
+  // Reference max m_ref (log2 units) that p, l and O are taken against,
+  // m_sub = m_ref - bias, and thr = the raw score above which a row's tile max
+  // moves the reference: tau above it (-inf until the row has one).
+  float m_ref = -__builtin_inff();
+  float m_sub = 0.0f;
+  float thr = -__builtin_inff();
   float l_run = 0.0f;
+  const float inv_c = 1.0f / c;
   constexpr float masked_raw = -__builtin_inff();
   constexpr int kReadsPerOp = Op::DW / 4;
 
@@ -1081,15 +1093,26 @@ fa_fwd_dma_kernel(FwdArgs p) {
             s[b][r] = rel < lim ? s[b][r] : masked_raw;
           }
       }
+      // row max of the raw scores; a tile where no row's max exceeds the
+      // reference by more than tau takes p against the reference as it stands
       const float ext = swap_halves_max(max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; }));
-      const float m_new = vmax(m_run, ext * c);
-      // a causal chunk can start above a row's diagonal: until the row meets a
-      // valid key its max stays -inf, and a zero reference keeps p = 0, alpha = 0
-      float m_ref = m_new;
-      if constexpr (SPLIT && CAUSAL) m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      m_run = m_new;
-      const float m_sub = m_ref - kPBias;
+      float alpha = 1.0f;
+      if (__any(ext > thr)) {
+        // a new exact reference for every row of the wave, O rescaled to it
+        const float m_new = vmax(m_ref, ext * c);
+        // a causal chunk can start above a row's diagonal: until the row meets
+        // a valid key its reference stays -inf, and a zero subtrahend keeps
+        // p = 0 and alpha = 0
+        const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m_ref - m_use);
+        m_ref = m_new;
+        m_sub = m_use - kPBias;
+        thr = m_new == -__builtin_inff() ? -__builtin_inff() : (m_use + kTau) * inv_c;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -1098,12 +1121,6 @@ fa_fwd_dma_kernel(FwdArgs p) {
 #pragma unroll
       for (int i = 4; i < NB * 16; ++i) ps[i & 3] += s[i >> 4][i & 15];
       l_run = alpha * l_run + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
-      }
       Op pop[PV_STEPS];
 #pragma unroll
       for (int n = 0; n < PV_STEPS; ++n) {
@@ -1176,13 +1193,13 @@ fa_fwd_dma_kernel(FwdArgs p) {
 
   const float l_tot = swap_halves_sum(l_run);
   if constexpr (SPLIT) {
-    store_partial<MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_run - kPBias, dv);
+    store_partial<MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_ref - kPBias, dv);
     return;
   }
   const float inv = dv / l_tot;
   if (my_q < N) {
     if (hh == 0)
-      p.lse[(size_t)bh * N + my_q] = (m_run - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+      p.lse[(size_t)bh * N + my_q] = (m_ref - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
     const size_t obase = ((size_t)bh * N + my_q) * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
