@@ -18,7 +18,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers on the current HIP device. The
  *     caller allocates and owns them. The library allocates nothing, keeps no
- *     per-call state and never synchronises the host.
+ *     per-call state and never synchronises the host (fa_fwd_splitkv_static
+ *     alone uses memory of the library's own: a fixed device array).
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     once it is enqueued. Device faults surface at the caller's next
  *     synchronisation.
@@ -54,7 +55,8 @@ typedef enum {
   FA_ERR_ALIGN = -7,     /* a tensor pointer is not 16-byte aligned             */
   FA_ERR_HIP = -8,       /* the HIP runtime rejected a launch                   */
   FA_ERR_WORKSPACE = -9, /* split-KV workspace NULL, misaligned or too small    */
-  FA_ERR_SPLITS = -10    /* num_splits / num_parts outside 1..FA_MAX_SPLITS     */
+  FA_ERR_SPLITS = -10,   /* num_splits / num_parts outside 1..FA_MAX_SPLITS     */
+  FA_ERR_SCRATCH = -11   /* fa_fwd_splitkv_static: partials above FA_STATIC_SCRATCH_BYTES */
 } fa_status_t;
 
 /* Largest number of key chunks fa_fwd_splitkv and fa_merge_partials accept. */
@@ -270,6 +272,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, int causal, float scale, int dtype,
                    const float* descales, int num_splits, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the library's own device scratch behind fa_fwd_splitkv_static. */
+#define FA_STATIC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * fa_fwd_splitkv_static -- fa_fwd_splitkv with its partials in the library's
+ * own device memory instead of a caller's workspace. For callers that cannot
+ * allocate device memory around the call (code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc): the call
+ * itself allocates nothing.
+ *
+ *   q ... num_splits  as fa_fwd_splitkv (same layouts, dtypes, validation
+ *                     and error codes, in the same order), then
+ *                     FA_ERR_SCRATCH when
+ *                     fa_splitkv_workspace_bytes(B, H, N, d, num_splits)
+ *                     exceeds FA_STATIC_SCRATCH_BYTES (64 MiB: e.g. 8 heads
+ *                     of 4096 tokens, d = 128, in 3 chunks); nothing is
+ *                     enqueued then.
+ *
+ * The scratch is a fixed array in the library's device code: every device the
+ * library runs on holds 64 MiB of it until the process ends, and the first
+ * call on a device looks up its address there (FA_ERR_HIP if that fails).
+ * Every call on one device shares that device's scratch: calls on the same
+ * stream are ordered, calls that overlap on one device (other streams, other
+ * threads without ordering) race on it. Nothing in it needs clearing: each
+ * call writes every partial the merge reads. O and L as fa_fwd_splitkv
+ * computes them, bit for bit.
+ */
+int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, int causal, float scale, int dtype,
+                          const float* descales, int num_splits, hipStream_t stream);
 
 /*
  * fa_merge_partials -- merge attention results computed over disjoint sets of

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_gqa",
-                                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_merge_partials", "fa_quantize_fp8", "fa_quantize_fp8_rotated",
+                                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_static", "fa_merge_partials", "fa_quantize_fp8", "fa_quantize_fp8_rotated",
                                      "fa_quantize_mxfp8_keys", "fa_quantize_mxfp8_rows",
                                      "fa_splitkv_chunk_keys", "fa_splitkv_default_splits",
                                      "fa_splitkv_workspace_bytes", "fa_status_string"]
@@ -59,6 +59,8 @@ def test_binding_constants_match_header():
     assert st == fa.STATUS
     m = re.search(r"#define\s+FA_MAX_SPLITS\s+(\d+)", _header_text())
     assert m and int(m.group(1)) == fa.FA_MAX_SPLITS
+    m = re.search(r"#define\s+FA_STATIC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", _header_text())
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.STATIC_SCRATCH_BYTES
 
 
 def test_status_strings(lib):
@@ -237,6 +239,36 @@ def _split(lib, num_splits=2, ws=WS, ws_bytes=1 << 40, **kw):
 ])
 def test_splitkv_validation_codes(lib, kw, code):
     assert _split(lib, **kw) == code
+
+
+def _split_static(lib, num_splits=2, **kw):
+    p = dict(q=A, k=A, v=A, o=A2, lse=A2, B=1, H=1, N=128, d=128, causal=0, scale=0.1, dtype=1,
+             descales=None)
+    p.update(kw)
+    return lib.fa_fwd_splitkv_static(p["q"], p["k"], p["v"], p["o"], p["lse"], p["B"], p["H"], p["N"],
+                                     p["d"], p["causal"], p["scale"], p["dtype"], p["descales"],
+                                     num_splits, None)
+
+
+# the partials of B*H*N rows in S chunks take 4*S*B*H*N*(d+1) bytes; 64 MiB holds
+# 8 heads of 4096 tokens in 3 chunks (50.7 MB) but not in 4 (67.6 MB)
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), -2), (dict(dtype=5), -3), (dict(d=32), -4), (dict(scale=float("nan")), -5),
+    (dict(dtype=2), -6), (dict(q=None), -1), (dict(k=MIS), -7), (dict(o=MIS), -7),
+    (dict(num_splits=0), -10), (dict(num_splits=65), -10), (dict(num_splits=-1), -10),
+    (dict(N=0), 0), (dict(H=0), 0), (dict(num_splits=0, N=0), -10),
+    (dict(H=8, N=4096, num_splits=4), -11),
+    (dict(H=56, N=30272, num_splits=2), -11),
+    (dict(B=1 << 20, H=1 << 12, N=4096), -2),
+])
+def test_splitkv_static_validation_codes(lib, kw, code):
+    assert _split_static(lib, **kw) == code
+
+
+def test_static_scratch_limit_is_the_documented_size(lib):
+    # the largest accepted problem needs at most FA_STATIC_SCRATCH_BYTES
+    assert lib.fa_splitkv_workspace_bytes(1, 8, 4096, 128, 3) <= fa.STATIC_SCRATCH_BYTES
+    assert lib.fa_splitkv_workspace_bytes(1, 8, 4096, 128, 4) > fa.STATIC_SCRATCH_BYTES
 
 
 def _merge(lib, op=A, lp=A2, S=2, B=1, H=1, N=16, d=128, out_dtype=1, o=WS, lse=A2):

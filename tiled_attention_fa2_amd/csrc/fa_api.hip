@@ -3,9 +3,11 @@
 // and merge entry points (the quantisers are in fa_quant_api.hip, the backward
 // in fa_bwd_api.hip). The declarations and the contract of every entry point
 // are in include/fa.h.
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_api_common.hpp"
@@ -168,6 +170,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: split-KV workspace missing, misaligned or too small";
     case FA_ERR_SPLITS: return "FA_ERR_SPLITS: number of splits / parts must be 1..FA_MAX_SPLITS";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the partials need more than the library's static scratch (FA_STATIC_SCRATCH_BYTES)";
     default: return "unknown fa status";
   }
 }
@@ -307,4 +311,57 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
   if (num_splits == 0) num_splits = -1;   // 0 selects the unsplit path inside run_fwd
   return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, num_splits,
                  workspace, workspace_bytes, stream);
+}
+
+// Scratch of fa_fwd_splitkv_static: the split-KV partials of one call, in the
+// library's own device memory, so that the call allocates nothing. Every
+// device the library runs on holds its own copy from the first use of the
+// library there until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: host code only ever passes the
+// per-device address taken below.
+static __device__ __align__(256) unsigned char scratch[FA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int H, int N, int d, int causal, float scale, int dtype,
+                                     const float* descales, int num_splits, hipStream_t stream) {
+  // the argument errors of fa_fwd_splitkv, in its order, before the scratch check
+  fa::FwdArgs a;
+  bool empty = false;
+  const int st = prepare_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, a, empty);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+  if (empty) return FA_OK;
+  const size_t need = fa_splitkv_workspace_bytes(B, H, N, d, num_splits);
+  if (need > (size_t)FA_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int r = scratch_address(&ws);
+  if (r != FA_OK) return r;
+  return run_fwd(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, descales, nullptr, num_splits, ws,
+                 (size_t)FA_STATIC_SCRATCH_BYTES, stream);
 }

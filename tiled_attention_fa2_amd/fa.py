@@ -22,8 +22,10 @@ DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 FA_OK = 0
 STATUS = {0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_DTYPE",
           -4: "FA_ERR_HEAD_DIM", -5: "FA_ERR_SCALE", -6: "FA_ERR_DESCALES",
-          -7: "FA_ERR_ALIGN", -8: "FA_ERR_HIP", -9: "FA_ERR_WORKSPACE", -10: "FA_ERR_SPLITS"}
+          -7: "FA_ERR_ALIGN", -8: "FA_ERR_HIP", -9: "FA_ERR_WORKSPACE", -10: "FA_ERR_SPLITS",
+          -11: "FA_ERR_SCRATCH"}
 FA_MAX_SPLITS = 64
+STATIC_SCRATCH_BYTES = 64 << 20   # FA_STATIC_SCRATCH_BYTES
 
 _lib = None
 
@@ -64,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.fa_splitkv_default_splits.restype = i
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
         L.fa_fwd_splitkv.restype = i
+        L.fa_fwd_splitkv_static.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp]
+        L.fa_fwd_splitkv_static.restype = i
         L.fa_merge_partials.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, vp]
         L.fa_merge_partials.restype = i
         L.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp, sz, vp]
@@ -234,6 +238,44 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descales=None
                1 if causal else 0, float(scale), code, ds, int(num_splits), _ptr(workspace), ws_bytes)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fwd_splitkv_static(q, k, v, num_splits: int, causal: bool = False, scale: float | None = None,
+                       descales=None, out=None, lse=None):
+    """The split-KV forward with its partials in the library's own static
+    device scratch (fa_fwd_splitkv_static): no workspace, and the C call
+    allocates nothing. q, k, v: contiguous [B, H, N, d] device tensors (no
+    grouped-query form), dtypes and descales as fwd; out and lse may be given
+    so that nothing is allocated here either. Raises FAError (FA_ERR_SCRATCH)
+    when the partials exceed STATIC_SCRATCH_BYTES."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if k.shape[1] != H:
+        raise ValueError("fwd_splitkv_static takes as many key/value heads as query heads")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = torch.float32 if code == DTYPE_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_out(out, odt, (B, H, N, d), "out")
+    _check_out(lse, torch.float32, (B, H, N), "lse")
+    ds = None
+    if code == DTYPE_FP8_E4M3:
+        if descales is None:
+            raise ValueError("FP8 inputs need descales (q, k, v per head)")
+        if descales.dtype != torch.float32 or descales.numel() != 3 * B * H \
+                or not descales.is_contiguous() or not descales.is_cuda:
+            raise ValueError("descales must be a contiguous float32 device tensor of 3*B*H values")
+        ds = _ptr(descales)
+    dev = _device(q, k, v, out, lse, descales)
+    st = _call("fa_fwd_splitkv_static", dev, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+               1 if causal else 0, float(scale), code, ds, int(num_splits))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitkv_static")
     return out, lse
 
 
