@@ -57,7 +57,7 @@ def kernel_name(w, num_splits: int = 1) -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only if
+    """L2-miss (fabric) bytes per launch from the committed rocprofv3 --pmc summary, only if
     it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_traffic.json")
     if not os.path.exists(path):
@@ -66,7 +66,7 @@ def measured_traffic(workload: str):
         t = json.load(f)
     if t.get("source_sha256") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("fabric_bytes_per_launch")
 
 
 def measured_mfma(workload: str):

@@ -40,11 +40,11 @@ def test_traffic_is_reported_only_for_the_source_it_was_taken_on(monkeypatch):
         rec = json.load(f)
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["source_sha256"])
     t = bench.measured_traffic(name)
-    assert t == rec["hbm_bytes_per_launch"]
+    assert t == rec["fabric_bytes_per_launch"]
     # read + write, each a counter scaled by the copy calibration
-    assert t == rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
-    assert rec["hbm_read_bytes"] == pytest.approx(rec["fetch_size_kib"] * 1024 * rec["fetch_scale"], rel=1e-6)
-    assert rec["hbm_write_bytes"] == pytest.approx(rec["write_size_kib"] * 1024 * rec["write_scale"], rel=1e-6)
+    assert t == rec["fabric_read_bytes"] + rec["fabric_write_bytes"]
+    assert rec["fabric_read_bytes"] == pytest.approx(rec["fetch_size_kib"] * 1024 * rec["fetch_scale"], rel=1e-6)
+    assert rec["fabric_write_bytes"] == pytest.approx(rec["write_size_kib"] * 1024 * rec["write_scale"], rel=1e-6)
     # HBM traffic can not be below the algorithmic bytes (Q, K, V read, O, L written once)
     assert t >= rec["algorithmic_bytes"]
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
