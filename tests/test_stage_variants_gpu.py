@@ -1,10 +1,10 @@
 """Determinism across pipeline depths: the race detector.
 
 The forward kernel fa_fwd launches (head dim 128, bf16 and FP8) is built again
-by tests/hip/stage_variants.hip with 2 and 3 LDS stages and with MFMA operand
-reads 1 and 2 steps ahead. None of these changes which values are added in
-which order; they change only when K/V tiles land in LDS and when operands are
-read. So every variant must reproduce fa_fwd's O and L bit for bit: a missing
+by tests/hip/stage_variants.hip with 2 and 3 LDS stages, with MFMA operand
+reads 1 and 2 steps ahead, and with each tile's prefetch issued before or after
+its QK MFMAs. None of these changes which values are added in which order;
+they change only when K/V tiles land in LDS and when operands are read. So every variant must reproduce fa_fwd's O and L bit for bit: a missing
 wait or barrier (a tile read before it landed, or overwritten while a slower
 wave still reads it) would show up as a difference.
 """
@@ -30,7 +30,8 @@ def _lib():
     lib = ctypes.CDLL(LIB)
     lib.fa_test_fwd_variant.restype = ctypes.c_int
     lib.fa_test_fwd_variant.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
-                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
     return lib
 
 
@@ -52,12 +53,16 @@ def test_pipeline_depth_and_lookahead_are_bitwise_neutral(dtype, causal):
     stream = torch.cuda.current_stream().cuda_stream
     for nstage in (2, 3):
         for look in (1, 2):
-            print(f"[case] {dtype} causal={causal} stages={nstage} look-ahead={look}", flush=True)
-            o = torch.empty_like(o_ref)
-            lse = torch.empty_like(l_ref)
-            rc = lib.fa_test_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                         B, H, N, int(causal), scale, code,
-                                         desc.data_ptr() if desc is not None else None, nstage, look, stream)
-            assert rc == 0, rc
-            torch.cuda.synchronize()
-            assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), (dtype, causal, nstage, look)
+            for late in (0, 1):
+                print(f"[case] {dtype} causal={causal} stages={nstage} look-ahead={look} late prefetch={late}",
+                      flush=True)
+                o = torch.empty_like(o_ref)
+                lse = torch.empty_like(l_ref)
+                rc = lib.fa_test_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                             lse.data_ptr(), B, H, N, int(causal), scale, code,
+                                             desc.data_ptr() if desc is not None else None, nstage, look, late,
+                                             stream)
+                assert rc == 0, rc
+                torch.cuda.synchronize()
+                assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), (dtype, causal, nstage, look, late)
+                assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), (dtype, causal, nstage, look, late)

@@ -827,8 +827,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // NSTAGE LDS stages: tile j lives in stage j % NSTAGE and is fetched
 // NSTAGE - 1 tiles ahead. WPE = waves per SIMD the registers must allow.
 // MX: per-block FP8 (E8M0 scales applied by the MFMAs, see FwdArgs).
+// LATE_DMA: the prefetch of each iteration is issued after the tile's QK
+// MFMAs instead of before them, so the K reads and MFMAs start right after
+// the barrier; the fetch then has one QK phase less to land, which a
+// three-stage ring absorbs and a two-stage one does not on long rows.
 template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2,
-          bool SPLIT = false, bool MX = false, int TAUQ = 0>
+          bool SPLIT = false, bool MX = false, int TAUQ = 0, bool LATE_DMA = false>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int D = 128;
@@ -1037,16 +1041,19 @@ fa_fwd_dma_kernel(FwdArgs p) {
   int buf = 0;   // stage of tile j
   for (int j = j_begin; j < j_end; ++j) {
     const int ahead = j + NSTAGE - 1;
-    if (ahead < j_end) {
-      int nb = buf + NSTAGE - 1;
-      nb = nb >= NSTAGE ? nb - NSTAGE : nb;
-      issue_tile(ahead, nb);
-    }
+    auto issue_ahead = [&]() {
+      if (ahead < j_end) {
+        int nb = buf + NSTAGE - 1;
+        nb = nb >= NSTAGE ? nb - NSTAGE : nb;
+        issue_tile(ahead, nb);
+      }
+    };
+    if constexpr (!LATE_DMA) issue_ahead();
     const int kbase = j * BN;
     const bool wave_active = !CAUSAL || kbase <= q0w + 31;
+    const unsigned char* st = smem + buf * STAGE;
+    f32x16 s[NB];
     if (wave_active) {
-      const unsigned char* st = smem + buf * STAGE;
-      f32x16 s[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -1076,7 +1083,9 @@ fa_fwd_dma_kernel(FwdArgs p) {
           }
         }
       if constexpr (LOOK > 0) interleave_reads_with_mfma<QK_STEPS * NB, kReadsPerOp, LOOK>();
-
+    }
+    if constexpr (LATE_DMA) issue_ahead();
+    if (wave_active) {
       const bool need_mask = (kbase + BN > N) || (CAUSAL && kbase + BN - 1 > q0w);
       if (need_mask) {
         asm volatile("" ::: "memory");
