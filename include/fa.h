@@ -369,10 +369,16 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  *   d           64 or 128.   causal, scale: as in the forward.
  *   dtype       FA_DTYPE_BF16 only (anything else: FA_ERR_DTYPE).
  *   workspace   device memory owned by the caller, 16-byte aligned, at least
- *               fa_bwd_workspace_bytes(B, Hq, N) bytes: per query row the pair
- *               (L log2 e, D) in float. Calls sharing it must not overlap.
- * Enqueues three kernels (the (L, D) pass, then dK/dV and dQ). dQ is formed in
- * its own pass over the key tiles, without atomics: the result is
+ *               fa_bwd_workspace_bytes(B, Hq, N) bytes, that function asked
+ *               with the device the call runs on current: per query row the
+ *               pair (L log2 e, D) in float, and on grids too small to give
+ *               every compute unit two dQ workgroups (B*Hq*ceil(N/128) below
+ *               twice the CU count, N >= 2048) the fp32 partial dQ of S key
+ *               chunks (S = 2..8, no chunk under 1024 keys). Calls sharing it
+ *               must not overlap.
+ * Enqueues three kernels (the (L, D) pass, then dK/dV and dQ), and a fourth
+ * that sums the dQ partials in chunk order when the keys are chunked. dQ is
+ * formed in its own pass over the key tiles, without atomics: the result is
  * deterministic. All tensor pointers 16-byte aligned.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);

@@ -68,6 +68,26 @@ def test_backward_matches_oracle(d, causal):
         _check(q, k, v, do, causal, 1.0 / math.sqrt(d), label=f"N={N} d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_dq_key_split(d, causal):
+    # grids too small for two dQ workgroups per CU cut the keys into chunks of
+    # >= 1024 whose partial dQ are summed in order: 2 x 2500 tokens takes 2
+    # chunks, 2 x 3333 (ragged) 3 on a 256-CU device
+    for B, H, N in [(1, 2, 2500), (1, 2, 3333)]:
+        assert fa.bwd_workspace_bytes(B, H, N) > 8 * B * H * N, "the key split is not taken"
+        q, k, v = make_qkv(B, H, N, d, "bf16", seed=N + d + 5)
+        do = make_dout(B, H, N, d, seed=N + d + 6)
+        _check(q, k, v, do, causal, 1.0 / math.sqrt(d), label=f"dQ key split N={N} d={d}")
+    # deterministic: the partials are summed in chunk order
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, num_splits=1)
+    a = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    b = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_gqa(causal):
     q, k, v = make_gqa(1, 8, 2, 400, 128, "bf16", seed=3)

@@ -46,11 +46,11 @@ def rule(tmp_path_factory):
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
 
-    def run(cases):
+    def run(cases, which=0):
         inp = "".join(f"{w} {n} {c} {cus}\n" for w, n, c, cus in cases)
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, timeout=60)
         assert out.returncode == 0
-        return [int(x) for x in out.stdout.split()]
+        return [int(line.split()[which]) for line in out.stdout.splitlines()]
     return run
 
 
@@ -75,3 +75,20 @@ def test_invariants(rule):
             assert (s - 1) * w < (3 if c else 2) * cus
     # degenerate arguments
     assert rule([(0, 4096, 0, 256), (256, 0, 0, 256), (256, 4096, 0, 0)]) == [1, 1, 1]
+
+
+def test_backward_dq_split_rule(rule):
+    # the dQ pass (two waves per SIMD): 8 heads x 4096 tokens is 256 workgroups,
+    # one per CU of a 256-CU device, so two chunks of 2048 keys
+    dq = lambda cases: rule(cases, which=1)
+    assert dq([(256, 4096, 0, 256), (2048, 2048, 1, 256), (13272, 30272, 0, 256)]) == [2, 1, 1]
+    cases = [(w, n, c, cus) for w in (1, 7, 64, 128, 255, 256, 300, 511, 512, 513, 5000)
+             for n in (1, 100, 1023, 1024, 2047, 4096, 30272, 1 << 20) for c in (0, 1) for cus in (80, 256, 304)]
+    for (w, n, c, cus), s in zip(cases, dq(cases)):
+        assert 1 <= s <= 8
+        if w >= 2 * cus:
+            assert s == 1                      # already two workgroups per CU
+        if s > 1:
+            assert n // s >= 1024              # no chunk under 1024 keys
+            assert (s - 1) * w < 2 * cus       # the fewest chunks that reach two per CU
+    assert dq([(0, 4096, 0, 256), (256, 0, 0, 256), (256, 4096, 0, 0)]) == [1, 1, 1]

@@ -41,4 +41,22 @@ inline int default_splits(long long wgs, long long N, bool causal, long long cus
   return (int)(s < 1 ? 1 : s);
 }
 
+// Key chunks of the backward's dQ pass, given its wgs = B*H*ceil(N/128)
+// workgroups and the device's CUs: one when the grid already gives every CU
+// two workgroups (two waves per SIMD, what the dQ kernel is built for); else
+// the fewest chunks that reach two per CU, no chunk under 1024 keys, at most 8.
+// The partial dQ of every chunk goes through the workspace
+// (fa_bwd_workspace_bytes).
+#ifndef FA_DQ_MAX_SPLITS
+#define FA_DQ_MAX_SPLITS 8
+#endif
+inline int bwd_dq_splits(long long wgs, long long N, long long cus) {
+  if (wgs <= 0 || N <= 0 || cus <= 0 || wgs >= 2 * cus) return 1;
+  long long s = ceil_div(2 * cus, wgs);
+  const long long by_keys = N / 1024 > 1 ? N / 1024 : 1;
+  if (s > by_keys) s = by_keys;
+  if (s > FA_DQ_MAX_SPLITS) s = FA_DQ_MAX_SPLITS;
+  return (int)(s < 1 ? 1 : s);
+}
+
 }  // namespace fa_api

@@ -14,9 +14,27 @@ using fa_api::aligned16;
 using fa_api::aligned4;
 using fa_api::ceil_div;
 
+namespace {
+
+// Bytes of the (L, D) pairs, rounded up so that the dQ partials after them
+// start 256-byte aligned.
+size_t ld_bytes(long long BH, long long N) { return ((size_t)8 * (size_t)BH * (size_t)N + 255) & ~(size_t)255; }
+
+// Key chunks of the dQ pass on the current device (1: no split).
+int dq_splits(long long BH, long long N) {
+  const int cus = fa_api::device_cus();
+  return fa_api::bwd_dq_splits(BH * ceil_div(N, fa::bwd::kRows), N, cus);
+}
+
+}  // namespace
+
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 0 || N < 0) return 0;
-  return (size_t)8 * (size_t)B * (size_t)H * (size_t)N;
+  const long long BH = (long long)B * H;
+  const int S = dq_splits(BH, N);
+  if (S <= 1) return (size_t)8 * (size_t)BH * (size_t)N;
+  // the dQ partials, sized for head dim 128
+  return ld_bytes(BH, N) + (size_t)S * (size_t)BH * (size_t)N * 128 * 4;
 }
 
 // 32-key blocks per wave of the dK/dV kernel (each wave reads its Q / dO
@@ -76,9 +94,17 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   // `group` query heads: the same rule with group * d bytes per row
   a.causal_order_kv = fa_api::causal_order(BH / a.group, 1, N, (long long)d * a.group, 2);
   a.scale = scale;
-  const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles)),
-      g_dkdv((unsigned)(BH / a.group * a.n_ktiles));
+  // dQ key split on grids that leave the SIMDs with fewer than two waves
+  const int S = dq_splits(BH, N);
+  a.dq_splits = S;
+  a.dq_chunk_tiles = (int)ceil_div(ceil_div(N, 32), S);
+  a.dq_part = S > 1 ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + ld_bytes(BH, N)) : nullptr;
+  if (BH * n_tiles * S > INT_MAX) return FA_ERR_SHAPE;
+  const long long merge_blocks = ceil_div(BH * N, 256 / (d / 8));
+  const dim3 blk(256), g_pre((unsigned)pre_blocks), g_dq((unsigned)(BH * n_tiles * S)),
+      g_dkdv((unsigned)(BH / a.group * a.n_ktiles)), g_merge((unsigned)merge_blocks);
   const bool c = causal != 0;
+  const bool split = S > 1;
   if (d == 128) {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<128>, g_pre, blk, 0, stream, a);
     if (c) {
@@ -86,13 +112,23 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, 1, 1>), g_dkdv, blk, 0, stream, a);
       else
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, true, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true>), g_dq, blk, 0, stream, a);
+      if (split) {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true, true>), g_dq, blk, 0, stream, a);
+        hipLaunchKernelGGL(fa::fa_bwd_dq_merge_kernel<128>, g_merge, blk, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, true>), g_dq, blk, 0, stream, a);
+      }
     } else {
       if (one_block)
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, 1, 1>), g_dkdv, blk, 0, stream, a);
       else
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<128, false, kDkdvKB, 1>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false>), g_dq, blk, 0, stream, a);
+      if (split) {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false, true>), g_dq, blk, 0, stream, a);
+        hipLaunchKernelGGL(fa::fa_bwd_dq_merge_kernel<128>, g_merge, blk, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<128, false>), g_dq, blk, 0, stream, a);
+      }
     }
   } else {
     hipLaunchKernelGGL(fa::fa_bwd_pre_kernel<64>, g_pre, blk, 0, stream, a);
@@ -101,13 +137,23 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, 1, 1>), g_dkdv, blk, 0, stream, a);
       else
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, true, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true>), g_dq, blk, 0, stream, a);
+      if (split) {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true, true>), g_dq, blk, 0, stream, a);
+        hipLaunchKernelGGL(fa::fa_bwd_dq_merge_kernel<64>, g_merge, blk, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, true>), g_dq, blk, 0, stream, a);
+      }
     } else {
       if (one_block)
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, 1, 1>), g_dkdv, blk, 0, stream, a);
       else
         hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<64, false, kDkdvKB, kDkdvKB>), g_dkdv, blk, 0, stream, a);
-      hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false>), g_dq, blk, 0, stream, a);
+      if (split) {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false, true>), g_dq, blk, 0, stream, a);
+        hipLaunchKernelGGL(fa::fa_bwd_dq_merge_kernel<64>, g_merge, blk, 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<64, false>), g_dq, blk, 0, stream, a);
+      }
     }
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -63,6 +63,13 @@ struct BwdArgs {
   int causal_order;     // order of the dQ kernel's causal tiles (work_item)
   int causal_order_kv;  // order of the dK/dV kernel's causal key blocks (work_item, flipped)
   float scale;
+  // dQ key split (kernels instantiated with SPLIT): chunk s of a query tile
+  // takes the 32-key tiles [s * dq_chunk_tiles, (s + 1) * dq_chunk_tiles) and
+  // writes its unscaled fp32 partial dQ to dq_part[s]; fa_bwd_dq_merge_kernel
+  // sums the parts in order.
+  int dq_splits;
+  int dq_chunk_tiles;
+  float* dq_part;       // [dq_splits][BH][N][D] fp32
 };
 
 // D = rowsum(dO * O) in fp32 and L in log2 units, one row per D/8 lanes.
@@ -223,7 +230,11 @@ __device__ __forceinline__ void store_rows(void* out, size_t row, int hh, const 
 constexpr int kDqLook = FA_DQ_LOOK;   // MFMA steps of LDS reads in flight
 
 // dQ: one workgroup per (batch * query head, 128 queries); waves own 32 rows.
-template <int D, bool CAUSAL>
+// SPLIT: one workgroup per (batch * query head, 128 queries, key chunk), for
+// grids that would otherwise leave the SIMDs with fewer than two waves ("Kernels
+// and Memory in LLM Inference", section "Flash-Decoding: one token, whole
+// chip": the keys cut into chunks whose partial results are summed after).
+template <int D, bool CAUSAL, bool SPLIT = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_bwd_dq_kernel(BwdArgs p) {
   using S = bwd::Shape<D>;
@@ -236,8 +247,16 @@ fa_bwd_dq_kernel(BwdArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
 
-  int bh, qt;
-  work_item(blockIdx.x, p.BH * p.n_tiles, p.n_tiles, CAUSAL ? p.causal_order : 0, bh, qt);
+  int bh, qt, sp = 0;
+  if constexpr (SPLIT) {
+    int t;
+    work_item(blockIdx.x, p.BH * p.n_tiles * p.dq_splits, p.n_tiles * p.dq_splits, CAUSAL ? p.causal_order : 0,
+              bh, t);
+    qt = t / p.dq_splits;
+    sp = t - qt * p.dq_splits;
+  } else {
+    work_item(blockIdx.x, p.BH * p.n_tiles, p.n_tiles, CAUSAL ? p.causal_order : 0, bh, qt);
+  }
   const int N = p.N;
   const int q0 = qt * bwd::kRows;
   const int q0w = q0 + 32 * wave;
@@ -274,6 +293,11 @@ fa_bwd_dq_kernel(BwdArgs p) {
     const int last = (q0 + bwd::kRows - 1) / 32 + 1;
     T = T < last ? T : last;
   }
+  int j_begin = 0, j_end = T;
+  if constexpr (SPLIT) {
+    j_begin = sp * p.dq_chunk_tiles;
+    j_end = j_begin + p.dq_chunk_tiles < T ? j_begin + p.dq_chunk_tiles : T;
+  }
 
   const int dma_row = (64 * wave + lane) / S::CPR;
   const int dma_pc = lane % S::CPR;
@@ -292,12 +316,12 @@ fa_bwd_dq_kernel(BwdArgs p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[mb][r] = 0.0f;
 
-  issue(0, 0);
+  if (j_begin < j_end) issue(j_begin, j_begin & 1);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int j = 0; j < T; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     const int buf = j & 1;
-    if (j + 1 < T) issue(j + 1, buf ^ 1);
+    if (j + 1 < j_end) issue(j + 1, buf ^ 1);
     const int kbase = j * 32;
     const bool wave_active = !CAUSAL || kbase <= q0w + 31;
     if (wave_active) {
@@ -357,7 +381,49 @@ fa_bwd_dq_kernel(BwdArgs p) {
     wait_vmcnt<0>();
     __syncthreads();
   }
-  if (my_q < N) bwd::store_rows<MB>(p.dq, (size_t)bh * N + my_q, hh, dq, p.scale);
+  if (my_q < N) {
+    if constexpr (SPLIT) {
+      // the chunk's unscaled partial, zero where the chunk has no tile
+      float* dst = p.dq_part + (((size_t)sp * p.BH + bh) * (size_t)N + my_q) * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * mb + 8 * jj + 4 * hh;
+          *(float4*)(dst + d0) = make_float4(dq[mb][4 * jj + 0], dq[mb][4 * jj + 1], dq[mb][4 * jj + 2],
+                                             dq[mb][4 * jj + 3]);
+        }
+    } else {
+      bwd::store_rows<MB>(p.dq, (size_t)bh * N + my_q, hh, dq, p.scale);
+    }
+  }
+}
+
+// dQ of the key split: scale * (part 0 + part 1 + ...), summed in chunk order
+// (deterministic), to bf16. One row of D values per D/8 lanes, 8 each.
+template <int D>
+__global__ void __launch_bounds__(256) fa_bwd_dq_merge_kernel(BwdArgs p) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const long long rows = (long long)p.BH * p.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  const int c0 = 8 * (threadIdx.x % TPR);
+  const size_t stride = (size_t)rows * D;
+  const float* src = p.dq_part + (size_t)row * D + c0;
+  float4 a = *(const float4*)src, b = *(const float4*)(src + 4);
+  for (int s = 1; s < p.dq_splits; ++s) {
+    const float4 x = *(const float4*)(src + s * stride), y = *(const float4*)(src + s * stride + 4);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  }
+  const float m = p.scale;
+  uint4 pk;
+  pk.x = pack_bf16(a.x * m, a.y * m);
+  pk.y = pack_bf16(a.z * m, a.w * m);
+  pk.z = pack_bf16(b.x * m, b.y * m);
+  pk.w = pack_bf16(b.z * m, b.w * m);
+  *(uint4*)((unsigned short*)p.dq + (size_t)row * D + c0) = pk;
 }
 
 // ---------------------------------------------------------------------------

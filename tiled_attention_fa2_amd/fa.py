@@ -497,7 +497,9 @@ def fwd_mxfp8(q, k, v, scales, causal: bool = False, scale: float | None = None,
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
-    """Device workspace bytes fa_bwd needs (8 per query row)."""
+    """Device workspace bytes fa_bwd needs on the current device: 8 per query
+    row, plus the fp32 partial dQ of its key chunks on grids too small to fill
+    the device."""
     return int(lib().fa_bwd_workspace_bytes(int(B), int(H), int(N)))
 
 
