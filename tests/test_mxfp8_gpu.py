@@ -194,8 +194,12 @@ def test_unit_scales_match_the_per_head_kernel():
     # of the same e4m3 values. With magnitudes 0.5 .. 1.875 (codes 0x30-0x3F)
     # every product is a multiple of 2^-8 and every score sum stays below 2^9,
     # so S is exact in fp32 in either kernel's summation order, and the rest
-    # of the arithmetic is the same: the outputs agree bit for bit.
-    B, H, N, d = 1, 2, 300, 128
+    # of the arithmetic is the same: the outputs agree bit for bit. The heads
+    # are enough for the per-head forward to take its narrow tiles (more than
+    # two workgroups per CU), which are the per-block kernel's tiles.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, d = 300, 128
+    B, H = 1, (2 * cus) // ((N + 127) // 128) + 1
     g = torch.Generator().manual_seed(11)
     codes = [(torch.randint(0x30, 0x40, (B, H, N, d), generator=g) |
               (torch.randint(0, 2, (B, H, N, d), generator=g) << 7)).to(torch.uint8) for _ in range(3)]

@@ -1,20 +1,31 @@
 """Determinism across pipeline depths: the race detector.
 
-The forward kernel fa_fwd launches (head dim 128, bf16 and FP8) is built again
-by tests/hip/stage_variants.hip with 2 and 3 LDS stages, with MFMA operand
-reads 1 and 2 steps ahead, and with each tile's prefetch issued before or after
-its QK MFMAs. None of these changes which values are added in which order;
-they change only when K/V tiles land in LDS and when operands are read. So every variant must reproduce fa_fwd's O and L bit for bit: a missing
-wait or barrier (a tile read before it landed, or overwritten while a slower
-wave still reads it) would show up as a difference.
+The forward kernel fa_fwd launches at head dim 128 (bf16 and FP8), in both of
+its tile configurations (narrow: key tile 32 / 64, three waves per SIMD, for
+full grids; wide: 64 / 128, two waves per SIMD, for grids of at most two
+workgroups per CU), is built again by tests/hip/stage_variants.hip with 2 and
+3 LDS stages, with MFMA operand reads 1 and 2 steps ahead, and with each
+tile's prefetch issued before or after its QK MFMAs. None of these changes
+which values are added in which order; they change only when K/V tiles land in
+LDS and when operands are read. So every variant must reproduce the library's
+own configuration bit for bit: a missing wait or barrier (a tile read before
+it landed, or overwritten while a slower wave still reads it) would show up as
+a difference.
+
+Each baseline is also held to the oracle (bf16: 1e-2 plus the bf16 floor;
+FP8: the per-element bounds), on ragged and one-key shapes, and must equal
+fa_fwd bit for bit on a grid for which fa_fwd picks that configuration.
 """
 import ctypes
 import math
 import os
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
+from fp8_bounds import assert_fp8
 from tiled_attention_fa2_amd import fa
 from tiled_attention_fa2_amd.inputs import make_qkv
 
@@ -22,6 +33,11 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "tests", "hip", "libstage_variants.so")
+# the library's configurations: (dtype, causal, wide) -> (stages, look-ahead, late prefetch)
+LIBRARY = {("bf16", False, 0): (3, 2, 1), ("bf16", True, 0): (3, 2, 1),
+           ("fp8", False, 0): (2, 2, 0), ("fp8", True, 0): (2, 2, 1),
+           ("bf16", False, 1): (2, 2, 1), ("bf16", True, 1): (2, 2, 1),
+           ("fp8", False, 1): (2, 2, 0), ("fp8", True, 1): (2, 2, 1)}
 
 
 def _lib():
@@ -31,38 +47,96 @@ def _lib():
     lib.fa_test_fwd_variant.restype = ctypes.c_int
     lib.fa_test_fwd_variant.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_void_p]
+                                        ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("causal", [False, True])
-def test_pipeline_depth_and_lookahead_are_bitwise_neutral(dtype, causal):
-    lib = _lib()
-    B, H, N, d = 2, 3, 1000, 128       # ragged last tile; causal: the order across heads too
-    scale = 1.0 / math.sqrt(d)
-    q, k, v = (t.cuda().contiguous() for t in make_qkv(B, H, N, d, "bf16", seed=21))
+def _inputs(dtype, B, H, N, seed):
+    q, k, v = (t.cuda().contiguous() for t in make_qkv(B, H, N, 128, "bf16", seed=seed))
     if dtype == "fp8":
         q, k, v, ds = fa.quantize_qkv_fp8(q, k, v)
-        code, desc = fa.DTYPE_FP8_E4M3, ds.contiguous()
-        o_ref, l_ref = fa.fwd(q, k, v, causal=causal, scale=scale, descales=desc, num_splits=1)
-    else:
-        code, desc = fa.DTYPE_BF16, None
-        o_ref, l_ref = fa.fwd(q, k, v, causal=causal, scale=scale, num_splits=1)
+        return (q, k, v), ds.contiguous()
+    return (q, k, v), None
+
+
+def _variant(lib, qkv, desc, dtype, causal, scale, wide, nstage, look, late):
+    q, k, v = qkv
+    B, H, N, _ = q.shape
+    o = torch.empty((B, H, N, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    code = fa.DTYPE_FP8_E4M3 if dtype == "fp8" else fa.DTYPE_BF16
+    rc = lib.fa_test_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N,
+                                 int(causal), scale, code, desc.data_ptr() if desc is not None else None, nstage,
+                                 look, late, wide, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, rc
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream().cuda_stream
+    return o, lse
+
+
+def _check_oracle(o, lse, qkv, desc, dtype, causal, scale, label):
+    B, H = qkv[0].shape[:2]
+    if dtype == "fp8":
+        ds = desc.cpu().numpy().reshape(3, B, H)
+        ref_in = tuple(oracle.dequantize_per_head(t.cpu().numpy(), ds[i]) for i, t in enumerate(qkv))
+        O, L = oracle.attention(*ref_in, scale=scale, causal=causal)
+        assert_fp8(o.float().cpu().numpy(), lse.cpu().numpy(), O, L, ref_in, scale, causal=causal, label=label)
+    else:
+        ref_in = tuple(t.double().cpu().numpy() for t in qkv)
+        O, L = oracle.attention(*ref_in, scale=scale, causal=causal)
+        floor = float(np.max(np.abs(torch.from_numpy(O).to(torch.bfloat16).double().numpy() - O)))
+        assert np.max(np.abs(o.double().cpu().numpy() - O)) <= 1e-2 + floor, label
+        assert np.max(np.abs(lse.double().cpu().numpy() - L)) <= 1e-3, label
+
+
+@pytest.mark.parametrize("wide", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_pipeline_depth_and_lookahead_are_bitwise_neutral(dtype, causal, wide):
+    lib = _lib()
+    B, H, N = 2, 3, 1000               # ragged last tile; causal: the order across heads too
+    scale = 1.0 / math.sqrt(128)
+    qkv, desc = _inputs(dtype, B, H, N, seed=21)
+    base = LIBRARY[(dtype, causal, wide)]
+    o_ref, l_ref = _variant(lib, qkv, desc, dtype, causal, scale, wide, *base)
+    _check_oracle(o_ref, l_ref, qkv, desc, dtype, causal, scale, f"{dtype} causal={causal} wide={wide}")
     for nstage in (2, 3):
         for look in (1, 2):
             for late in (0, 1):
-                print(f"[case] {dtype} causal={causal} stages={nstage} look-ahead={look} late prefetch={late}",
-                      flush=True)
-                o = torch.empty_like(o_ref)
-                lse = torch.empty_like(l_ref)
-                rc = lib.fa_test_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                             lse.data_ptr(), B, H, N, int(causal), scale, code,
-                                             desc.data_ptr() if desc is not None else None, nstage, look, late,
-                                             stream)
-                assert rc == 0, rc
-                torch.cuda.synchronize()
-                assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), (dtype, causal, nstage, look, late)
-                assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), (dtype, causal, nstage, look, late)
+                print(f"[case] {dtype} causal={causal} wide={wide} stages={nstage} look-ahead={look} "
+                      f"late prefetch={late}", flush=True)
+                o, lse = _variant(lib, qkv, desc, dtype, causal, scale, wide, nstage, look, late)
+                key = (dtype, causal, wide, nstage, look, late)
+                assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), key
+                assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), key
+
+
+@pytest.mark.parametrize("wide", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_both_configurations_on_edge_shapes(dtype, wide):
+    # one key, a single partial tile, one tile plus one key, causal and not
+    lib = _lib()
+    scale = 0.3
+    for N in (1, 33, 129):
+        qkv, desc = _inputs(dtype, 1, 2, N, seed=N)
+        for causal in (False, True):
+            o, lse = _variant(lib, qkv, desc, dtype, causal, scale, wide, *LIBRARY[(dtype, causal, wide)])
+            _check_oracle(o, lse, qkv, desc, dtype, causal, scale, f"{dtype} N={N} causal={causal} wide={wide}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_baselines_are_the_library(dtype):
+    # fa_fwd picks the wide tiles for a grid of at most two workgroups per CU
+    # and the narrow ones above; compared on the unsplit path
+    lib = _lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 1000
+    scale = 1.0 / math.sqrt(128)
+    for H, wide in ((3, 1), ((2 * cus) // ((N + 127) // 128) + 1, 0)):
+        qkv, desc = _inputs(dtype, 1, H, N, seed=22)
+        assert (H * ((N + 127) // 128) <= 2 * cus) == bool(wide)
+        o_ref, l_ref = _variant(lib, qkv, desc, dtype, False, scale, wide, *LIBRARY[(dtype, False, wide)])
+        kw = dict(descales=desc) if dtype == "fp8" else {}
+        o, lse = fa.fwd(*qkv, scale=scale, num_splits=1, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), (dtype, H, wide)
+        assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), (dtype, H, wide)

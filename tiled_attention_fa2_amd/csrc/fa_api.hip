@@ -28,32 +28,56 @@ constexpr int kWaves = 4;
 constexpr int kWavesPerSimd = 2;
 
 // Head dim 128, bf16 and fp8: global -> LDS by DMA, V^T read with the LDS
-// transpose reads (the shapes the DiT benchmark runs). bf16: key tile 32,
-// three stages, three waves per SIMD; fp8: key tile 64, two stages, three
-// waves per SIMD.
-// MX: per-block FP8 scales (fp8 only), same tiles as plain fp8.
-template <int DT, bool CAUSAL, bool SPLIT, bool MX = false>
+// transpose reads. Two tile configurations:
+//   narrow: key tile 32 (bf16, three stages) / 64 (fp8, two stages), three
+//           waves per SIMD, three workgroups per CU (48 / 32 KB of LDS);
+//   wide:   key tile 64 (bf16) / 128 (fp8), two stages (64 KB), two waves per
+//           SIMD, two workgroups per CU.
+// Wide runs grids of at most two workgroups per CU, where a third slot per CU
+// would stay empty: the wider tile halves the per-tile barrier, max, rescale
+// test and DMA work. Measured (same box, medians, L2 flushed): 8 x 4096 bf16
+// split in 2 +6%, unsplit +20%, FP8 +7% / +14%, 16 x 2048 bf16 +18%; on full
+// grids the third wave per SIMD is worth more (56 x 30272 bf16 -4.7%, a
+// 768-workgroup grid -2%).
+// MX: per-block FP8 scales (fp8 only), narrow tiles.
+template <int DT, bool CAUSAL, bool SPLIT, bool MX, bool WIDE>
 void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
-  constexpr int BN = DT == fa::kBF16 ? 32 : 64;
-  constexpr int NSTAGE = DT == fa::kBF16 ? 3 : 2;
-  constexpr int LOOK = 2, WPE = 3;
+  constexpr int BN = DT == fa::kBF16 ? (WIDE ? 64 : 32) : (WIDE ? 128 : 64);
+  constexpr int NSTAGE = DT == fa::kBF16 && !WIDE ? 3 : 2;
+  constexpr int LOOK = 2, WPE = WIDE ? 2 : 3;
+  static_assert(!(MX && WIDE), "per-block FP8 runs the narrow tiles");
   // FP8: the reference max may lag the running max by 0.75 (log2 units)
   constexpr int TAUQ = DT == fa::kFP8 ? 3 : 0;
-  // prefetch after the QK MFMAs: bf16 (three stages) and causal per-head FP8
-  // (measured +2-5% there; FP8 non-causal, two stages, loses 2-4%; causal
-  // per-block FP8 would spill)
+  // prefetch after the QK MFMAs: bf16 and causal per-head FP8 (measured +2-5%
+  // there; FP8 non-causal loses 2-4%; causal per-block FP8 would spill)
   constexpr bool LATE = DT == fa::kBF16 || (CAUSAL && !MX);
   const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
   hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX, TAUQ, LATE>),
                      dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
 }
 
+template <int DT, bool MX, bool WIDE>
+void launch_fwd_dma_cfg(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
+  if (causal)
+    split ? launch_fwd_dma_inst<DT, true, true, MX, WIDE>(a, stream)
+          : launch_fwd_dma_inst<DT, true, false, MX, WIDE>(a, stream);
+  else
+    split ? launch_fwd_dma_inst<DT, false, true, MX, WIDE>(a, stream)
+          : launch_fwd_dma_inst<DT, false, false, MX, WIDE>(a, stream);
+}
+
 template <int DT, bool MX = false>
 int launch_fwd_dma(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
-  if (causal)
-    split ? launch_fwd_dma_inst<DT, true, true, MX>(a, stream) : launch_fwd_dma_inst<DT, true, false, MX>(a, stream);
-  else
-    split ? launch_fwd_dma_inst<DT, false, true, MX>(a, stream) : launch_fwd_dma_inst<DT, false, false, MX>(a, stream);
+  const long long items = (long long)a.BH * a.n_qtiles * (split ? a.n_splits : 1);
+  const int cus = fa_api::device_cus();
+  if constexpr (MX) {
+    launch_fwd_dma_cfg<DT, true, false>(a, causal, split, stream);
+  } else {
+    if (cus > 0 && items <= 2LL * cus)
+      launch_fwd_dma_cfg<DT, false, true>(a, causal, split, stream);
+    else
+      launch_fwd_dma_cfg<DT, false, false>(a, causal, split, stream);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
