@@ -239,9 +239,10 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits);
  * fa_splitkv_default_splits -- the num_splits this library picks for a shape
  * on the current device, with C compute units and W = B*H*ceil(N/128)
  * workgroups of fa_fwd: 1 when W >= 2C; else ceil(2C / W) (non-causal) or
- * ceil(3C / W) (causal), at most N / 1024 (no chunk under 1024 keys; N / 2048
- * for a non-causal grid with W >= C) and at most 16. Always returns a value >= 1 (1 for invalid arguments or a failed
- * device query).
+ * ceil(3C / W) (causal), at most N / 1024 (no chunk under 1024 keys; for a
+ * non-causal grid with W >= C, N / 2048, or N / 4096 when dtype is
+ * FA_DTYPE_FP8_E4M3) and at most 16. Always returns a value >= 1 (1 for
+ * invalid arguments or a failed device query).
  */
 int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype);
 

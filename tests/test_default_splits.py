@@ -18,6 +18,16 @@ Measured TFLOP/s per number of chunks (best marked *):
   fp8  d128 32 x 1024:  1 772* | 2 482 | 3 470
   fp8  d128  4 x 4096:  3 718 | 4 776* | 6 744
   bf16 d64  causal 8 x 4096:  2 298 | 3 370* | 4 279
+With the wide tiles (two waves per SIMD) on grids of at most two workgroups
+per CU, re-measured (medians of 100 launches, L2 flushed):
+  bf16 d128  8 x 4096:  1 682 | 2 743* | 3 694 | 4 655
+  bf16 d128 causal 8 x 4096: 1 361 | 2 425 | 3 449* | 4 371
+  bf16 d128  4 x 8192:  1 745 | 2 860* | 3 820
+  bf16 d128  2 x 16384: 1 818 | 2 941* | 3 914
+  fp8  d128  8 x 4096:  1 1142* | 2 1084 | 3 1029
+  fp8  d128  4 x 8192:  1 1318 | 2 1392* | 3 1308
+  fp8  d128  2 x 16384: 1 1429 | 2 1588* | 3 1533
+  fp8  d128 causal 8 x 4096: 1 592 | 2 579 | 3 619*
 """
 import os
 import shutil
@@ -47,30 +57,40 @@ def rule(tmp_path_factory):
     assert r.returncode == 0, r.stderr[-2000:]
 
     def run(cases, which=0):
-        inp = "".join(f"{w} {n} {c} {cus}\n" for w, n, c, cus in cases)
+        inp = "".join(f"{c_[0]} {c_[1]} {c_[2]} {c_[3]} {c_[4] if len(c_) > 4 else 0}\n" for c_ in cases)
         out = subprocess.run([exe], input=inp, capture_output=True, text=True, timeout=60)
         assert out.returncode == 0
         return [int(line.split()[which]) for line in out.stdout.splitlines()]
     return run
 
 
+# FP8 (w, N, causal) -> chunks: a non-causal grid one deep keeps chunks of
+# >= 4096 keys
+MEASURED_FP8 = {(256, 4096, 0): 1, (256, 8192, 0): 2, (256, 16384, 0): 2, (256, 4096, 1): 3, (512, 1024, 0): 1}
+
+
 def test_choice_on_the_measured_shapes(rule):
     keys = list(MEASURED)
     got = rule([(w, n, c, 256) for w, n, c in keys])
     assert dict(zip(keys, got)) == MEASURED
+    keys = list(MEASURED_FP8)
+    got = rule([(w, n, c, 256, 1) for w, n, c in keys])
+    assert dict(zip(keys, got)) == MEASURED_FP8
 
 
 def test_invariants(rule):
-    cases = [(w, n, c, cus) for w in (1, 7, 64, 128, 255, 256, 300, 511, 512, 513, 5000)
-             for n in (1, 100, 1023, 1024, 2047, 4096, 30272, 1 << 20) for c in (0, 1) for cus in (80, 256, 304)]
-    for (w, n, c, cus), s in zip(cases, rule(cases)):
+    cases = [(w, n, c, cus, f) for w in (1, 7, 64, 128, 255, 256, 300, 511, 512, 513, 5000)
+             for n in (1, 100, 1023, 1024, 2047, 4096, 30272, 1 << 20) for c in (0, 1) for cus in (80, 256, 304)
+             for f in (0, 1)]
+    for (w, n, c, cus, f), s in zip(cases, rule(cases)):
         assert 1 <= s <= 16
         if w >= 2 * cus:
             assert s == 1                          # the device is already full
         if s > 1:
             assert n // s >= 1024                  # no chunk under 1024 keys
             if not c and w >= cus:
-                assert n // s >= 2048              # nor under 2048 on a grid already one deep
+                # nor under 2048 (bf16) / 4096 (FP8) on a grid already one deep
+                assert n // s >= (4096 if f else 2048)
             # the fewest chunks that reach two (three if causal) workgroups per CU
             assert (s - 1) * w < (3 if c else 2) * cus
     # degenerate arguments

@@ -291,12 +291,12 @@ extern "C" size_t fa_splitkv_workspace_bytes(int B, int H, int N, int d, int num
 }
 
 extern "C" int fa_splitkv_default_splits(int B, int H, int N, int d, int causal, int dtype) {
-  (void)dtype;
   if (B <= 0 || H <= 0 || N <= 0) return 1;
   if (d != 64 && d != 128) return 1;
   const int cus = fa_api::device_cus();
   if (cus <= 0) return 1;
-  return fa_api::default_splits((long long)B * H * ceil_div(N, kBM), N, causal != 0, cus);
+  return fa_api::default_splits((long long)B * H * ceil_div(N, kBM), N, causal != 0, cus,
+                                dtype == FA_DTYPE_FP8_E4M3);
 }
 
 extern "C" int fa_merge_partials(const float* o_parts, const float* lse_parts, int num_parts,

@@ -26,15 +26,16 @@ inline int causal_order(long long BH, long long group, long long N, long long d,
 // compute units, given wgs = B*H*ceil(N/128) unsplit workgroups: none once
 // there are two workgroups per CU; else enough chunks for about two per CU
 // (non-causal) or three (causal, whose uneven per-tile work needs more pieces
-// to balance), never a chunk under 1024 keys, nor under 2048 when a
-// non-causal grid already has a workgroup on every CU; at most 16. Measured on
-// MI355X (bf16 and FP8 at d = 128, bf16 at d = 64): filling every slot instead
-// cost up to 26% (32 heads x 1024 tokens, chunks of 341 keys), splitting 512
-// workgroups cost 7-11%, and 16 x 2048 lost 3.6% with chunks of 1024 keys.
-inline int default_splits(long long wgs, long long N, bool causal, long long cus) {
+// to balance), never a chunk under 1024 keys, nor, when a non-causal grid
+// already has a workgroup on every CU, under 2048 (bf16) or 4096 (FP8) keys;
+// at most 16. Measured on MI355X (bf16 and FP8 at d = 128, bf16 at d = 64):
+// filling every slot instead cost up to 26% (32 heads x 1024 tokens, chunks of
+// 341 keys), splitting 512 workgroups cost 7-11%, 16 x 2048 lost 3.6% with
+// chunks of 1024 keys, and FP8 8 x 4096 (wide tiles unsplit) 5% in 2 chunks.
+inline int default_splits(long long wgs, long long N, bool causal, long long cus, bool fp8 = false) {
   if (wgs <= 0 || N <= 0 || cus <= 0 || wgs >= 2 * cus) return 1;
   long long s = ceil_div((causal ? 3 : 2) * cus, wgs);
-  const long long min_keys = (!causal && wgs >= cus) ? 2048 : 1024;
+  const long long min_keys = (!causal && wgs >= cus) ? (fp8 ? 4096 : 2048) : 1024;
   const long long by_keys = N / min_keys > 1 ? N / min_keys : 1;
   if (s > by_keys) s = by_keys;
   if (s > 16) s = 16;
