@@ -34,10 +34,10 @@ pytestmark = pytest.mark.gpu
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "tests", "hip", "libstage_variants.so")
 # the library's configurations: (dtype, causal, wide) -> (stages, look-ahead, late prefetch)
-LIBRARY = {("bf16", False, 0): (3, 2, 1), ("bf16", True, 0): (3, 2, 1),
-           ("fp8", False, 0): (2, 2, 0), ("fp8", True, 0): (2, 2, 1),
-           ("bf16", False, 1): (2, 2, 1), ("bf16", True, 1): (2, 2, 1),
-           ("fp8", False, 1): (2, 2, 0), ("fp8", True, 1): (2, 2, 1)}
+LIBRARY = {("bf16", False, 0): (3, 2, 0), ("bf16", True, 0): (3, 2, 0),
+           ("fp8", False, 0): (2, 2, 0), ("fp8", True, 0): (2, 2, 0),
+           ("bf16", False, 1): (2, 2, 0), ("bf16", True, 1): (2, 2, 0),
+           ("fp8", False, 1): (2, 2, 0), ("fp8", True, 1): (2, 2, 0)}
 
 
 def _lib():

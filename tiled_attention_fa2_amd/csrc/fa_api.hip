@@ -48,9 +48,9 @@ void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
   static_assert(!(MX && WIDE), "per-block FP8 runs the narrow tiles");
   // FP8: the reference max may lag the running max by 0.75 (log2 units)
   constexpr int TAUQ = DT == fa::kFP8 ? 3 : 0;
-  // prefetch after the QK MFMAs: bf16 and causal per-head FP8 (measured +2-5%
-  // there; FP8 non-causal loses 2-4%; causal per-block FP8 would spill)
-  constexpr bool LATE = DT == fa::kBF16 || (CAUSAL && !MX);
+  // the prefetch goes out before the QK MFMAs (issuing it after them was
+  // measured no faster on any shape, and 2-4% slower for FP8 non-causal)
+  constexpr bool LATE = false;
   const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
   hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX, TAUQ, LATE>),
                      dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
