@@ -27,18 +27,11 @@ __device__ __forceinline__ uint32_t merge_pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, m_bf16x2));
 }
 
-// o_part [S][rows][D], lse_part [S][rows] -> o [rows][D] (fp32 or bf16), lse [rows]
+// One row of the merge: lane c4 (of D/4) of row `row` (of `rows`).
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(256) fa_merge_kernel(const float* __restrict__ o_part,
-                                                       const float* __restrict__ lse_part, int S,
-                                                       long long rows, void* __restrict__ o,
-                                                       float* __restrict__ lse) {
-  constexpr int TPR = D / 4;          // lanes per row
-  constexpr int RPB = 256 / TPR;      // rows per workgroup
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c4 = threadIdx.x % TPR;
-  if (row >= rows) return;
-
+__device__ __forceinline__ void merge_row(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                          int S, long long rows, long long row, int c4, void* __restrict__ o,
+                                          float* __restrict__ lse) {
   float M = -__builtin_inff();
   for (int s = 0; s < S; ++s) M = fmaxf(M, lse_part[(size_t)s * rows + row]);
   float z = 0.0f;
@@ -67,6 +60,19 @@ __global__ void __launch_bounds__(256) fa_merge_kernel(const float* __restrict__
     ((uint2*)((unsigned short*)o + (size_t)row * D))[c4] = pk;
   }
   if (c4 == 0) lse[row] = z > 0.0f ? M + logf(z) : -__builtin_inff();
+}
+
+// o_part [S][rows][D], lse_part [S][rows] -> o [rows][D] (fp32 or bf16), lse [rows]
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(256) fa_merge_kernel(const float* __restrict__ o_part,
+                                                       const float* __restrict__ lse_part, int S,
+                                                       long long rows, void* __restrict__ o,
+                                                       float* __restrict__ lse) {
+  constexpr int TPR = D / 4;          // lanes per row
+  constexpr int RPB = 256 / TPR;      // rows per workgroup
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  merge_row<D, OUT_F32>(o_part, lse_part, S, rows, row, threadIdx.x % TPR, o, lse);
 }
 
 }  // namespace fa
