@@ -35,10 +35,10 @@ constexpr int kWavesPerSimd = 2;
 //           SIMD, two workgroups per CU.
 // Wide runs grids of at most two workgroups per CU, where a third slot per CU
 // would stay empty: the wider tile halves the per-tile barrier, max, rescale
-// test and DMA work. Measured (same box, medians, L2 flushed): 8 x 4096 bf16
-// split in 2 +6%, unsplit +20%, FP8 +7% / +14%, 16 x 2048 bf16 +18%; on full
-// grids the third wave per SIMD is worth more (56 x 30272 bf16 -4.7%, a
-// 768-workgroup grid -2%).
+// test and DMA work. Measured against the narrow tiles (same box, medians, L2
+// flushed, timing order alternated): unsplit 8 x 4096 bf16 +17%, FP8 +14%,
+// 16 x 2048 +16%, 4 x 8192 +17%; on full grids the third wave per SIMD is
+// worth more (56 x 30272 bf16 -4.7%, a 768-workgroup grid -2%).
 // MX: per-block FP8 scales (fp8 only), narrow tiles.
 template <int DT, bool CAUSAL, bool SPLIT, bool MX, bool WIDE>
 void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
