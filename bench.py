@@ -50,9 +50,10 @@ def kernel_source_hash() -> str:
 
 
 def kernel_name(w, num_splits: int = 1) -> str:
-    """The kernel fa_fwd launches for this workload (head dim 128 bf16 / fp8
-    use the DMA + transpose-read kernel); with key chunks, the merge follows."""
-    k = "fa_fwd_dma_kernel" if (w.d == 128 and w.dtype in ("bf16", "fp8")) else "fa_fwd_kernel"
+    """The kernel fa_fwd launches for this workload (bf16 and fp8 use the DMA +
+    transpose-read kernel, fp32 the register-staged one); with key chunks, the
+    merge follows."""
+    k = "fa_fwd_dma_kernel" if w.dtype in ("bf16", "fp8") else "fa_fwd_kernel"
     return k + " + fa_merge_kernel" if num_splits > 1 else k
 
 
@@ -290,7 +291,7 @@ def main():
                      **counter_fields(w.name, traffic, kern_ms, splits == 1)},
     }
 
-    if not a.no_fp8 and w.dtype == "bf16" and w.name.startswith("bf16_dit"):
+    if not a.no_fp8 and w.name == "bf16_dit_b1_h56_n30272_d128":
         w8 = WORKLOADS["fp8_dit_b1_h56_n30272_d128"]
         print("[bench] timing fp8 leg", file=sys.stderr, flush=True)
         q8, k8, v8, ds = fa.quantize_qkv_fp8(qd, kd, vd)

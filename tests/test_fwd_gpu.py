@@ -95,7 +95,8 @@ def _check(q, k, v, dtype, causal, scale, rows=None, label="", extra=True, iid=T
 
 # ---------------------------------------------------------------- workloads
 SMALL = ["f32_b1_h1_n256_d64", "bf16_b1_h8_n4096_d128", "bf16_causal_b4_h32_n2048_d128"]
-LARGE = ["bf16_dit_b1_h56_n30272_d128", "fp8_dit_b1_h56_n30272_d128"]
+LARGE = ["bf16_dit_b1_h56_n30272_d128", "fp8_dit_b1_h56_n30272_d128",
+         "bf16_dit_b1_h56_n30272_d64", "fp8_dit_b1_h56_n30272_d64"]
 
 
 @pytest.mark.parametrize("name", SMALL)
@@ -114,7 +115,7 @@ def test_workload_sampled_rows(name):
         _check(q, k, v, w.dtype, w.causal, w.scale, rows=rows, label=name, extra=False)
         return
     # FP8: the codes the benchmark times come from the device quantiser; they
-    # must equal the oracle's byte for byte on the whole 56 x 30272 x 128 grid
+    # must equal the oracle's byte for byte on the whole 56 x 30272 grid
     # (codes and descales), and the forward on them is checked on the rows
     print(f"[case] {name}: device quantiser on the full grid, then sampled rows", flush=True)
     q8, k8, v8, ds = fa.quantize_qkv_fp8(*_dev(q, k, v))
@@ -152,11 +153,12 @@ def test_ragged_lengths(dtype, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
-def test_multi_tile_ragged_causal(dtype):
+@pytest.mark.parametrize("d", [64, 128])
+def test_multi_tile_ragged_causal(dtype, d):
     # several query and key tiles, with a ragged tail on both
-    q, k, v = make_qkv(1, 2, 1000, 128, dtype, seed=7)
-    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label="N=1000 causal")
-    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label="N=1000")
+    q, k, v = make_qkv(1, 2, 1000, d, dtype, seed=7)
+    _check(q, k, v, dtype, True, 1.0 / math.sqrt(d), label=f"N=1000 d={d} causal")
+    _check(q, k, v, dtype, False, 1.0 / math.sqrt(d), label=f"N=1000 d={d}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])

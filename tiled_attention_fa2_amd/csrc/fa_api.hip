@@ -21,14 +21,14 @@ using fa_api::aligned16;
 using fa_api::aligned4;
 using fa_api::ceil_div;
 
-// Tile shapes: 4 waves x 32 query rows per workgroup; key tile 64 (bf16, fp8)
-// or 32 (fp32); registers bounded so two workgroups share a CU (2 waves per
-// SIMD): a single wave per SIMD cannot keep the MFMA pipe busy.
+// Every kernel: 4 waves x 32 query rows per workgroup. The register-staged
+// kernel (fp32, d = 64 and 128) takes key tile 32, registers bounded so two
+// workgroups share a CU (2 waves per SIMD).
 constexpr int kWaves = 4;
 constexpr int kWavesPerSimd = 2;
 
-// Head dim 128, bf16 and fp8: global -> LDS by DMA, V^T read with the LDS
-// transpose reads. Two tile configurations:
+// bf16 and fp8: global -> LDS by DMA, V^T read with the LDS transpose reads.
+// Head dim 128 has two tile configurations:
 //   narrow: key tile 32 (bf16, three stages) / 64 (fp8, two stages), three
 //           waves per SIMD, three workgroups per CU (48 / 32 KB of LDS);
 //   wide:   key tile 64 (bf16) / 128 (fp8), two stages (64 KB), two waves per
@@ -40,43 +40,52 @@ constexpr int kWavesPerSimd = 2;
 // 16 x 2048 +16%, 4 x 8192 +17%; on full grids the third wave per SIMD is
 // worth more (56 x 30272 bf16 -4.7%, a 768-workgroup grid -2%).
 // MX: per-block FP8 scales (fp8 only), narrow tiles.
-template <int DT, bool CAUSAL, bool SPLIT, bool MX, bool WIDE>
+// Head dim 64 has one configuration, two stages of 32 KB: key tile 64 at four
+// waves per SIMD (bf16, about 120 registers) and 128 at three (fp8, about 152).
+// Half the Q and O registers of d = 128 leave room for twice the keys per
+// tile, which spreads the per-tile work of this VALU-bound head dim over more
+// scores. Measured against key tile 32 and against three stages at three
+// waves per SIMD (same box, medians, L2 flushed): bf16 56 x 30272 999 against
+// 959 / 975 TFLOP/s, 8 x 4096 +4% / +38%.
+template <int DT, int D, bool CAUSAL, bool SPLIT, bool MX, bool WIDE>
 void launch_fwd_dma_inst(const fa::FwdArgs& a, hipStream_t stream) {
-  constexpr int BN = DT == fa::kBF16 ? (WIDE ? 64 : 32) : (WIDE ? 128 : 64);
-  constexpr int NSTAGE = DT == fa::kBF16 && !WIDE ? 3 : 2;
-  constexpr int LOOK = 2, WPE = WIDE ? 2 : 3;
+  constexpr bool kB = DT == fa::kBF16;
+  constexpr int BN = D == 64 ? (kB ? 64 : 128) : kB ? (WIDE ? 64 : 32) : (WIDE ? 128 : 64);
+  constexpr int NSTAGE = D == 128 && kB && !WIDE ? 3 : 2;
+  constexpr int LOOK = 2, WPE = D == 64 ? (kB ? 4 : 3) : WIDE ? 2 : 3;
   static_assert(!(MX && WIDE), "per-block FP8 runs the narrow tiles");
+  static_assert(D == 128 || !WIDE, "head dim 64: one configuration");
   // FP8: the reference max may lag the running max by 0.75 (log2 units)
   constexpr int TAUQ = DT == fa::kFP8 ? 3 : 0;
   // the prefetch goes out before the QK MFMAs (issuing it after them was
   // measured no faster on any shape, and 2-4% slower for FP8 non-causal)
   constexpr bool LATE = false;
   const long long items = (long long)a.BH * a.n_qtiles * (SPLIT ? a.n_splits : 1);
-  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX, TAUQ, LATE>),
+  hipLaunchKernelGGL((fa::fa_fwd_dma_kernel<DT, BN, kWaves, CAUSAL, LOOK, WPE, NSTAGE, SPLIT, MX, TAUQ, LATE, D>),
                      dim3((unsigned)items), dim3(64 * kWaves), 0, stream, a);
 }
 
-template <int DT, bool MX, bool WIDE>
+template <int DT, int D, bool MX, bool WIDE>
 void launch_fwd_dma_cfg(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
   if (causal)
-    split ? launch_fwd_dma_inst<DT, true, true, MX, WIDE>(a, stream)
-          : launch_fwd_dma_inst<DT, true, false, MX, WIDE>(a, stream);
+    split ? launch_fwd_dma_inst<DT, D, true, true, MX, WIDE>(a, stream)
+          : launch_fwd_dma_inst<DT, D, true, false, MX, WIDE>(a, stream);
   else
-    split ? launch_fwd_dma_inst<DT, false, true, MX, WIDE>(a, stream)
-          : launch_fwd_dma_inst<DT, false, false, MX, WIDE>(a, stream);
+    split ? launch_fwd_dma_inst<DT, D, false, true, MX, WIDE>(a, stream)
+          : launch_fwd_dma_inst<DT, D, false, false, MX, WIDE>(a, stream);
 }
 
-template <int DT, bool MX = false>
+template <int DT, bool MX = false, int D = 128>
 int launch_fwd_dma(const fa::FwdArgs& a, bool causal, bool split, hipStream_t stream) {
   const long long items = (long long)a.BH * a.n_qtiles * (split ? a.n_splits : 1);
   const int cus = fa_api::device_cus();
-  if constexpr (MX) {
-    launch_fwd_dma_cfg<DT, true, false>(a, causal, split, stream);
+  if constexpr (MX || D == 64) {
+    launch_fwd_dma_cfg<DT, D, MX, false>(a, causal, split, stream);
   } else {
     if (cus > 0 && items <= 2LL * cus)
-      launch_fwd_dma_cfg<DT, false, true>(a, causal, split, stream);
+      launch_fwd_dma_cfg<DT, D, false, true>(a, causal, split, stream);
     else
-      launch_fwd_dma_cfg<DT, false, false>(a, causal, split, stream);
+      launch_fwd_dma_cfg<DT, D, false, false>(a, causal, split, stream);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -106,10 +115,10 @@ int launch_any(const fa::FwdArgs& a, int dtype, int d, bool split, bool mx, hipS
   switch (dtype) {
     case FA_DTYPE_BF16:
       return d == 128 ? launch_fwd_dma<fa::kBF16>(a, c, split, stream)
-                      : launch_fwd<fa::kBF16, 64, 64>(a, c, split, stream);
+                      : launch_fwd_dma<fa::kBF16, false, 64>(a, c, split, stream);
     case FA_DTYPE_FP8_E4M3:
       return d == 128 ? launch_fwd_dma<fa::kFP8>(a, c, split, stream)
-                      : launch_fwd<fa::kFP8, 64, 64>(a, c, split, stream);
+                      : launch_fwd_dma<fa::kFP8, false, 64>(a, c, split, stream);
     default:
       return d == 128 ? launch_fwd<fa::kF32, 128, 32>(a, c, split, stream)
                       : launch_fwd<fa::kF32, 64, 32>(a, c, split, stream);

@@ -1,5 +1,6 @@
-// FlashAttention-2 forward for gfx950 (MI355X), one kernel template for the
-// fp32, bf16 and FP8-e4m3 variants.
+// FlashAttention-2 forward for gfx950 (MI355X): fa_fwd_kernel (fp32, K/V
+// staged through registers) and fa_fwd_dma_kernel (bf16 and FP8-e4m3, K/V
+// fetched into LDS by DMA, further below).
 //
 // What it computes ("FlashAttention-2 from PyTorch to Triton", forward-pass
 // section and Triton kernel walkthrough; "1.8x Faster Attention on an RTX
@@ -27,11 +28,11 @@
 //     is baked into the LDS address where each V element is written (the
 //     "key order" idea of "1.8x Faster Attention on an RTX 5080", section
 //     "P stays in registers", moved from a prepare pass into the LDS store).
-//   * K/V tiles go global -> registers -> LDS, double buffered: the loads for
-//     tile j+1 are issued before tile j is computed and written to the other
-//     LDS buffer after it, one barrier per tile. V is stored transposed
-//     (feature-major) in LDS so every MFMA operand read is one contiguous
-//     16- or 32-byte LDS read. Rows are padded by 16 bytes so that eight
+//   * fa_fwd_kernel: K/V tiles go global -> registers -> LDS, double
+//     buffered: the loads for tile j+1 are issued before tile j is computed
+//     and written to the other LDS buffer after it, one barrier per tile. V
+//     is stored transposed (feature-major) in LDS so every MFMA operand read
+//     is one contiguous LDS read. Rows are padded by 16 bytes so that eight
 //     consecutive rows start in eight different 16-byte bank groups.
 //   * exp2 with scale*log2(e) folded into one FMA per score; masking only on
 //     tiles that hold keys >= N or straddle the causal diagonal; the causal
@@ -356,11 +357,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// v_perm_b32: byte k of the result is byte sel[k] of the 8-byte value {hi, lo}
-// (selectors 0-3 pick bytes of lo, 4-7 bytes of hi).
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -375,9 +371,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // two workgroups share a CU and one wave's softmax overlaps another's MFMAs.
 // LOOK > 0 pins the order of each run of MFMAs and their LDS operand reads,
 // with LOOK operands read ahead (0 leaves the order to the compiler).
+// The fp32 forward (true fp32 MFMA, v_mfma_f32_32x32x2_f32), any head dim the
+// host accepts (64, 128).
 template <int DT, int D, int BN, int NWAVES, bool CAUSAL, int WPE, int LOOK = 0, bool SPLIT = false>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_kernel(FwdArgs p) {
+  static_assert(DT == kF32, "register-staged kernel: fp32 (bf16 and FP8 run fa_fwd_dma_kernel)");
   using C = Cfg<DT, D, BN, NWAVES>;
   using Op = Operand<DT>;
   constexpr int ES = C::ES, KPL = C::KPL;
@@ -405,24 +404,8 @@ fa_fwd_kernel(FwdArgs p) {
   const unsigned char* Kg = (const unsigned char*)p.k + kv_off;
   const unsigned char* Vg = (const unsigned char*)p.v + kv_off;
 
-  // scale * log2(e), with the fp8 descales of Q and K folded in
+  // scale * log2(e)
   float c = p.scale * 1.4426950408889634f;
-  float dv = 1.0f;
-  if constexpr (DT == kFP8) {
-    c *= p.descales[bh] * p.descales[p.BH + bkv];
-    dv = p.descales[p.BH + p.BH / p.group + bkv];
-  }
-  // fp8 keeps P * 256 in e4m3's normal range ("1.8x Faster Attention on an
-  // RTX 5080", section "P goes through shared memory"): exp2(t + 8) = 256 exp2(t),
-  // folded into the subtraction of the running max at no cost.
-  constexpr float kPBias = DT == kFP8 ? 8.0f : 0.0f;
-  // Conditional rescale ("Kernels and Memory in LLM Inference", section
-  // "FlashAttention-4"): the reference max may move only when a tile's max
-  // beats it by more than kTau (log2 units), saving O rescales. It is kept at
-  // 0 (exact running max): with a stale reference the dominant weight of a
-  // near one-hot row is 2^delta instead of exactly 1, and its bf16 rounding
-  // adds up to 2^-9 |v| to the output error (measured on peaked inputs).
-  constexpr float kTau = 0.0f;
   // scale == 0: every valid score gets the same weight. A tiny positive c
   // gives exactly that (|s * c| < 2^-24, so exp2 rounds to 1) and lets a
   // masked score be -inf rather than -inf * 0 = NaN.
@@ -509,40 +492,13 @@ fa_fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int it = 0; it < C::VPT; ++it) {
         unsigned char* dst0 = st + v_soff + it * (C::NT / (BN / 4)) * C::EPC * C::VROW;
-        if constexpr (ES == 2) {
-          // element e of the chunk = half e%2 of dword e/2; four keys -> 8 bytes
+        // four keys land two positions apart
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
+        for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {
-              const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-              uint2 pk;
-              pk.x = perm(vst[it][1][w], vst[it][0][w], sel);
-              pk.y = perm(vst[it][3][w], vst[it][2][w], sel);
-              *(uint2*)(dst0 + (2 * w + hi) * C::VROW) = pk;
-            }
-        } else if constexpr (ES == 1) {
-          // 4x4 byte transpose of the four keys' dword w
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t t0 = perm(vst[it][1][w], vst[it][0][w], 0x05010400u);
-            const uint32_t t1 = perm(vst[it][3][w], vst[it][2][w], 0x05010400u);
-            const uint32_t t2 = perm(vst[it][1][w], vst[it][0][w], 0x07030602u);
-            const uint32_t t3 = perm(vst[it][3][w], vst[it][2][w], 0x07030602u);
-            *(uint32_t*)(dst0 + (4 * w + 0) * C::VROW) = perm(t1, t0, 0x05040100u);
-            *(uint32_t*)(dst0 + (4 * w + 1) * C::VROW) = perm(t1, t0, 0x07060302u);
-            *(uint32_t*)(dst0 + (4 * w + 2) * C::VROW) = perm(t3, t2, 0x05040100u);
-            *(uint32_t*)(dst0 + (4 * w + 3) * C::VROW) = perm(t3, t2, 0x07060302u);
-          }
-        } else {
-          // fp32: four keys land two positions apart
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              *(uint32_t*)(dst0 + e * C::VROW + (vt_pos<KPL>(4 * v_g + i) - vt_pos<KPL>(4 * v_g)) * 4) =
-                  vst[it][i][e];
-        }
+          for (int i = 0; i < 4; ++i)
+            *(uint32_t*)(dst0 + e * C::VROW + (vt_pos<KPL>(4 * v_g + i) - vt_pos<KPL>(4 * v_g)) * 4) =
+                vst[it][i][e];
       }
     }
   };
@@ -626,26 +582,22 @@ fa_fwd_kernel(FwdArgs p) {
         ext = swap_halves_min(ext);
       }
       // every processed (row, tile) pair holds at least one valid key, so
-      // m_tile is finite. The reference max moves only when this tile's max
-      // exceeds it by more than kTau (log2 units); until then p <= 2^kTau and
-      // O needs no rescale. l and O always share the reference, so the result
-      // is unchanged.
+      // m_tile is finite
       const float m_tile = ext * c;
-      const float m_new = m_tile > m_run + kTau ? vmax(m_run, m_tile) : m_run;
+      const float m_new = m_tile > m_run ? m_tile : m_run;
       // a causal chunk can start above a row's diagonal: until the row meets a
       // valid key its max stays -inf, and a zero reference keeps p = 0, alpha = 0
       float m_ref = m_new;
       if constexpr (SPLIT && CAUSAL) m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       m_run = m_new;
-      const float m_sub = m_ref - kPBias;
 
-      // p = exp2(s*c - m_ref) (times 256 for fp8)
+      // p = exp2(s*c - m_ref)
 #pragma unroll
       for (int b = 0; b < C::NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_sub));
+          s[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -m_ref));
       const float psum = tree_reduce<C::NB * 16>([&](int i) { return s[i >> 4][i & 15]; },
                                                  [](float x, float y) { return x + y; });
       l_run = alpha * l_run + psum;
@@ -661,32 +613,7 @@ fa_fwd_kernel(FwdArgs p) {
       // P^T operands, straight from the score registers
       Op pop[C::PV_STEPS];
 #pragma unroll
-      for (int n = 0; n < C::PV_STEPS; ++n) {
-        if constexpr (DT == kBF16) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int r0 = n * KPL + 2 * w;
-            pop[n].w[w] = pack_bf16(s[r0 >> 4][r0 & 15], s[(r0 + 1) >> 4][(r0 + 1) & 15]);
-          }
-        } else if constexpr (DT == kFP8) {
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int r0 = n * KPL + 4 * w;
-            // both halves are overwritten below: an opaque, unset word spares the
-            // v_mov that clearing it would cost
-            int v;
-            asm volatile("" : "=v"(v));
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[r0 >> 4][r0 & 15],
-                                                s[(r0 + 1) >> 4][(r0 + 1) & 15], v, false);
-            v = __builtin_amdgcn_cvt_pk_fp8_f32(s[(r0 + 2) >> 4][(r0 + 2) & 15],
-                                                s[(r0 + 3) >> 4][(r0 + 3) & 15], v, true);
-            pop[n].w[w] = (uint32_t)v;
-          }
-        } else {
-          const int r0 = n;
-          pop[n].w[0] = f2u(s[r0 >> 4][r0 & 15]);
-        }
-      }
+      for (int n = 0; n < C::PV_STEPS; ++n) pop[n].w[0] = f2u(s[n >> 4][n & 15]);
 
       // O^T += V^T P^T, the d-blocks alternating between consecutive MFMAs
 #pragma unroll
@@ -712,14 +639,13 @@ fa_fwd_kernel(FwdArgs p) {
   // ---- epilogue: full row sum, L, O / l, bounded stores ----
   const float l_tot = swap_halves_sum(l_run);
   if constexpr (SPLIT) {
-    store_partial<C::MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_run - kPBias, dv);
+    store_partial<C::MB>(p, sp, bh, my_q, hh, oacc, l_tot, m_run, 1.0f);
     return;
   }
-  const float inv = dv / l_tot;
+  const float inv = 1.0f / l_tot;
   if (my_q < N) {
     if (hh == 0)
-      p.lse[(size_t)bh * N + my_q] =
-          (m_run - kPBias + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
+      p.lse[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.6931471805599453f;
     const size_t obase = ((size_t)bh * N + my_q) * D;
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
@@ -728,21 +654,14 @@ fa_fwd_kernel(FwdArgs p) {
         const int d0 = 32 * mb + 8 * jj + 4 * hh;
         const float x0 = oacc[mb][4 * jj + 0] * inv, x1 = oacc[mb][4 * jj + 1] * inv;
         const float x2 = oacc[mb][4 * jj + 2] * inv, x3 = oacc[mb][4 * jj + 3] * inv;
-        if constexpr (DT == kF32) {
-          *(float4*)((float*)p.o + obase + d0) = make_float4(x0, x1, x2, x3);
-        } else {
-          uint2 pk;
-          pk.x = pack_bf16(x0, x1);
-          pk.y = pack_bf16(x2, x3);
-          *(uint2*)((unsigned short*)p.o + obase + d0) = pk;
-        }
+        *(float4*)((float*)p.o + obase + d0) = make_float4(x0, x1, x2, x3);
       }
   }
 }
 
 
 // ---------------------------------------------------------------------------
-// DMA variant (head dim 128, bf16 and fp8): K and V tiles go global -> LDS
+// DMA variant (bf16 and fp8, head dim 64 and 128): K and V tiles go global -> LDS
 // with buffer_load ... lds (no registers, no LDS store instructions, no
 // repacking), row-major with a 16-byte XOR swizzle per row, and the V^T MFMA
 // operands are read with the LDS transpose reads:
@@ -754,15 +673,33 @@ fa_fwd_kernel(FwdArgs p) {
 // Each transpose read therefore hands a lane 4 (bf16) or 8 (fp8) keys of one
 // feature, and the rows are chosen so that those keys are the ones the lane's
 // P^T slots hold (the same key order as vt_pos).
-// Swizzles (physical 16-byte chunk = logical chunk ^ f(row)):
-//   K: f = row & 7           -> the 8 rows an MFMA row-read touches at once
-//                               land in 8 different bank groups;
+// Swizzles (physical 16-byte chunk = logical chunk ^ f(row)), for the 64
+// banks of 4 bytes that serve a 128-bit read 16 lanes at a time and a 64-bit
+// read 32 lanes at a time:
+//   K, d = 128: f = row & 7  -> the 8 rows an MFMA row-read touches at once
+//                               land in 8 different bank groups (16 rows per
+//                               phase still meet twice);
+//   K, d = 64: bf16 f = (row >> 1) & 7 (two 128-byte rows per bank sweep),
+//              fp8 f = (row >> 2) & 3 (four 64-byte rows): the 16 rows of a
+//              phase fill all 16 bank groups;
 //   V bf16: f = 2 (row & 3)  -> the 4 rows x 32 bytes of a tr16 group hit
-//                               8 different bank groups;
-//   V fp8: f = (row & 3) | ((row >> 3) & 1) << 2 -> the same for tr8's
-//                               8 rows x 16 bytes.
-__device__ __forceinline__ int swz_v(int dt_fp8, int row) {
-  return dt_fp8 ? ((row & 3) | (((row >> 3) & 1) << 2)) : 2 * (row & 3);
+//                               8 different bank groups (at d = 64 the whole
+//                               32-lane phase is conflict-free);
+//   V fp8, d = 128: f = (row & 3) | ((row >> 3) & 1) << 2 -> the same for
+//                               tr8's 8 rows x 16 bytes;
+//   V fp8, d = 64: f = 2 ((row >> 3) & 1) (four chunks per row).
+// Each f depends on row bits 0-3 only, so rows 16 apart share it.
+template <int DT, int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 7;
+  else if constexpr (DT == kBF16) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int DT, int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (DT == kBF16) return 2 * (row & 3);
+  else if constexpr (D == 128) return (row & 3) | (((row >> 3) & 1) << 2);
+  else return 2 * ((row >> 3) & 1);
 }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -832,11 +769,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // the barrier; the fetch then has one QK phase less to land, which a
 // three-stage ring absorbs and a two-stage one does not on long rows.
 template <int DT, int BN, int NWAVES, bool CAUSAL, int LOOK, int WPE = 2, int NSTAGE = 2,
-          bool SPLIT = false, bool MX = false, int TAUQ = 0, bool LATE_DMA = false>
+          bool SPLIT = false, bool MX = false, int TAUQ = 0, bool LATE_DMA = false, int D = 128>
 __global__ void __launch_bounds__(64 * NWAVES) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fa_fwd_dma_kernel(FwdArgs p) {
-  constexpr int D = 128;
   static_assert(DT == kBF16 || DT == kFP8, "DMA variant: bf16 and fp8");
+  static_assert(D == 128 || (D == 64 && !MX), "head dim 128, or 64 without per-block scales");
   using Op = Operand<DT>;
   constexpr int ES = Traits<DT>::ES, KPL = Traits<DT>::KPL;
   constexpr int NT = 64 * NWAVES, BM = 32 * NWAVES;
@@ -853,8 +790,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int NINSTR = TILE / 1024 / NWAVES;   // 1 KB DMA instructions per wave per tile
   constexpr int ROWS_PER_INSTR = 64 / CPR;
   static_assert(TILE % (1024 * NWAVES) == 0, "tile must split into whole DMA instructions");
-  static_assert(CPR >= 8, "K swizzle needs at least 8 chunks per row");
-  constexpr int kFp8 = DT == kFP8 ? 1 : 0;
+  static_assert(CPR >= 4, "swizzles need at least 4 chunks per row");
 
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
   static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three stages");
@@ -952,10 +888,10 @@ fa_fwd_dma_kernel(FwdArgs p) {
   // buffer descriptor carries the rest.
   const int dma_row = (64 * wave + lane) / CPR;
   const int dma_pc = lane % CPR;
-  const uint32_t k_goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ (dma_row & 7));
-  const uint32_t v_goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ swz_v(kFp8, dma_row));
+  const uint32_t k_goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ swz_k<DT, D>(dma_row));
+  const uint32_t v_goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ swz_v<DT, D>(dma_row));
   constexpr int T_ROWS = 64 * NWAVES / CPR;      // rows between instruction t and t+1
-  static_assert(T_ROWS % 8 == 0, "swizzle period");
+  static_assert(T_ROWS % 16 == 0, "swizzle period");
 
   auto issue_tile = [&](int jt, int buf) {
     const int kbase = jt * BN;
@@ -982,11 +918,13 @@ fa_fwd_dma_kernel(FwdArgs p) {
   };
 
   // ---- MFMA operand read bases ----
-  // K: row r = 32b + l32 (r & 7 = l32 & 7); bf16 chunk 2kk + h, fp8 chunks 4kk + 2h + x
-  const int gk = l32 & 7;
-  uint32_t kb[4];
+  // K: row r = 32b + l32 (same swizzle as row l32); bf16 chunk 2kk + h, fp8
+  // chunks 4kk + 2h + x
+  const int gk = swz_k<DT, D>(l32);
+  constexpr int NKB = DT == kFP8 ? 2 * QK_STEPS : (QK_STEPS < 4 ? QK_STEPS : 4);
+  uint32_t kb[NKB];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NKB; ++u) {
     const int lc = DT == kFP8 ? (MX ? 4 * (u >> 1) + 2 * (u & 1) + hh : 4 * (u >> 1) + 2 * hh + (u & 1))
                               : (2 * u + hh);
     kb[u] = (uint32_t)l32 * ROW + 16 * (lc ^ gk);
@@ -1003,13 +941,13 @@ fa_fwd_dma_kernel(FwdArgs p) {
     const int x = 2 * va + (q >> 1);
 #pragma unroll
     for (int m1 = 0; m1 < 2; ++m1)
-      vb[m1] = TILE + (uint32_t)r0 * ROW + 16 * ((4 * m1 + x) ^ (2 * e)) + 8 * (q & 1);
+      vb[m1] = TILE + (uint32_t)r0 * ROW + 16 * ((4 * m1 + x) ^ swz_v<DT, D>(r0)) + 8 * (q & 1);
   } else {
     // source row 4h + e%4 + 8(e/4) (+ 16t), e = j/2; columns 32mb + 16a + 8q, q = j%2
     const int e = vj >> 1, q = vj & 1, r0 = 4 * hh + (e & 3) + 8 * (e >> 2);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      vb[mb] = TILE + (uint32_t)r0 * ROW + 16 * ((2 * mb + va) ^ e) + 8 * q;
+    for (int mb = 0; mb < MB; ++mb)
+      vb[mb] = TILE + (uint32_t)r0 * ROW + 16 * ((2 * mb + va) ^ swz_v<DT, D>(r0)) + 8 * q;
   }
 
   f32x16 oacc[MB];
