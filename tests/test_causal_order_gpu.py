@@ -27,8 +27,8 @@ pytestmark = pytest.mark.gpu
 B, H, N, D = 2, 8, 777, 128
 
 
-def _device_inputs(dtype):
-    q, k, v = make_qkv(B, H, N, D, dtype, seed=41)
+def _device_inputs(dtype, d=D):
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=41)
     if dtype != "fp8":
         return [t.cuda().contiguous() for t in (q, k, v)], None, (q, k, v)
     codes, ds = zip(*(oracle.quantize_per_head(t) for t in (q, k, v)))
@@ -40,10 +40,11 @@ def _device_inputs(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_causal_order_across_heads_forward(dtype, splits):
-    print(f"[case] causal order across heads, fwd dtype={dtype} B={B} H={H} N={N} splits={splits}", flush=True)
-    scale = 1.0 / math.sqrt(D)
-    dev, descales, ref_in = _device_inputs(dtype)
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_order_across_heads_forward(dtype, splits, d):
+    print(f"[case] causal order across heads, fwd dtype={dtype} B={B} H={H} N={N} d={d} splits={splits}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    dev, descales, ref_in = _device_inputs(dtype, d)
     kw = dict(causal=True, scale=scale, num_splits=splits)
     if descales is not None:
         kw["descales"] = descales
