@@ -55,6 +55,10 @@ WORKLOADS = {
         # key/value heads ("Kernels and Memory in LLM Inference", section
         # "Store less: MQA, GQA, MLA"; about 8 groups is the setting it names)
         Workload("bf16_gqa_b1_hq56_hkv8_n30272_d128", "bf16", 1, 56, 30272, 128, False, Hkv=8),
+        # one GPU's share of the DiT shape when its 56 heads are split over 8
+        # GPUs: 7 heads
+        Workload("bf16_dit_shard_b1_h7_n30272_d128", "bf16", 1, 7, 30272, 128, False),
+        Workload("fp8_dit_shard_b1_h7_n30272_d128", "fp8", 1, 7, 30272, 128, False),
         # the DiT shape at head dim 64 (the other head dim the library takes)
         Workload("bf16_dit_b1_h56_n30272_d64", "bf16", 1, 56, 30272, 64, False),
         Workload("fp8_dit_b1_h56_n30272_d64", "fp8", 1, 56, 30272, 64, False),
