@@ -127,3 +127,45 @@ def test_planted_mistake_in_the_bound_is_caught():
         fb.EPS_E4M3, fb.SIGMA_E4M3 = saved
     assert (np.abs(O_em - O_ref) / bO).max() <= 1.0
     assert (np.abs(O_em - O_ref) / bO_bad).max() > 1.0
+
+
+def _round_bf16(x):
+    """Round float64 values to bf16 (round to nearest, ties to even) through
+    float32, as the kernel's v_cvt_pk_bf16_f32 does with fp32 p."""
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _emulate_bf16(q, k, v, scale, causal):
+    """float64 emulation of the bf16 kernel's P rounding: exact running max,
+    p = 2^(s c - m) (the largest weight exactly 1), l over unrounded p, O over
+    bf16-rounded p. The reference max is the row's final max: rescales by
+    alpha = 2^(m_old - m_new) are applied to the rounded p of earlier tiles in
+    fp32 by the kernel, which does not change their relative error."""
+    B, H, N, d = q.shape
+    O = np.zeros((B, H, N, d))
+    c = scale * LOG2E
+    for b in range(B):
+        for h in range(H):
+            T = (q[b, h] @ k[b, h].T) * c
+            if causal:
+                T = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], T, -np.inf)
+            m = np.max(T, axis=1, keepdims=True)
+            p = np.exp2(T - m)
+            O[b, h] = (_round_bf16(p) @ v[b, h]) / p.sum(axis=1, keepdims=True)
+    return O
+
+
+@pytest.mark.parametrize("variant", ["outlier", "peaked"])
+def test_bf16_p_rounding_bound_holds_and_is_not_vacuous(variant):
+    # the bf16 stress tolerance term 2^-8 sum_j P_ij |v_jd| of the parity tests
+    from fp8_bounds import p_weighted_abs_v
+    q, k, v = (t.double().numpy() for t in make_qkv(1, 2, 257, 64, "bf16", seed=5, variant=variant))
+    scale = 1.0 / math.sqrt(64)
+    for causal in (False, True):
+        O_ref, L_ref = oracle.attention(q, k, v, scale=scale, causal=causal)
+        O_em = _emulate_bf16(q, k, v, scale, causal)
+        bound = 2.0 ** -8 * p_weighted_abs_v((q, k, v), scale, L_ref, causal=causal)
+        ratio = np.abs(O_em - O_ref) / np.maximum(bound, 1e-300)
+        assert ratio.max() <= 1.0, (variant, causal, ratio.max())
+        assert ratio.max() >= 0.05, (variant, causal, ratio.max())

@@ -25,7 +25,7 @@ import pytest
 import torch
 
 import oracle
-from fp8_bounds import assert_fp8
+from fp8_bounds import assert_fp8, p_weighted_abs_v
 from tiled_attention_fa2_amd import fa
 from tiled_attention_fa2_amd.inputs import WORKLOADS, make_qkv, sample_rows
 
@@ -88,7 +88,18 @@ def _check(q, k, v, dtype, causal, scale, rows=None, label="", extra=True, iid=T
             assert err_o <= TOL_O["fp8"] and err_l <= TOL_L and cos >= 0.999, (label, err_o, err_l, cos)
         return err_o, err_l, cos
     tol_o = TOL_O[dtype] + (floor if extra and dtype != "f32" else 0.0)
-    assert err_o <= tol_o, (label, err_o, tol_o)
+    if dtype == "bf16" and not iid:
+        # stress inputs (outlier channels, peaked rows): |v| far above 1 makes
+        # the bf16 rounding of P scale with it; element by element, the stated
+        # tolerance plus that rounding's worst case 2^-8 sum_j P_ij |v_jd|
+        bound = tol_o + 2.0 ** -8 * p_weighted_abs_v(ref_in, scale, L_ref, causal=causal, rows=rows)
+        ratio = np.abs(O_gpu - O_ref) / bound
+        i = np.unravel_index(np.argmax(ratio), ratio.shape)
+        print(f"    bf16 stress bound: largest dO/bound {ratio[i]:.3f} at (b,h,row,d)={tuple(int(x) for x in i)} "
+              f"(bound {bound[i]:.3e}, bounds {bound.min():.3e}..{bound.max():.3e})", flush=True)
+        assert ratio[i] <= 1.0, (label, err_o, bound[i])
+    else:
+        assert err_o <= tol_o, (label, err_o, tol_o)
     assert err_l <= TOL_L, (label, err_l, TOL_L)
     return err_o, err_l, cos
 
@@ -171,10 +182,11 @@ def test_scale_values(scale, dtype):
 
 @pytest.mark.parametrize("variant", ["peaked", "growing", "outlier"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_stress_inputs(variant, dtype):
-    q, k, v = make_qkv(1, 4, 2048, 128, dtype, seed=3, variant=variant)
-    _check(q, k, v, dtype, False, 1.0 / math.sqrt(128), label=f"stress {variant}", iid=False)
-    _check(q, k, v, dtype, True, 1.0 / math.sqrt(128), label=f"stress {variant} causal", iid=False)
+@pytest.mark.parametrize("d", [64, 128])
+def test_stress_inputs(variant, dtype, d):
+    q, k, v = make_qkv(1, 4, 2048, d, dtype, seed=3, variant=variant)
+    _check(q, k, v, dtype, False, 1.0 / math.sqrt(d), label=f"stress {variant} d={d}", iid=False)
+    _check(q, k, v, dtype, True, 1.0 / math.sqrt(d), label=f"stress {variant} d={d} causal", iid=False)
 
 
 # ----------------------------------------------------------------- invariants
