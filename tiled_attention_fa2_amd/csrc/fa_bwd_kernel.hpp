@@ -344,7 +344,7 @@ fa_bwd_dq_kernel(BwdArgs p) {
       // P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D); key kbase + 4hh + rel
       const bool need_mask = (kbase + 32 > N) || (CAUSAL && kbase + 31 > q0w);
       float ds[16];
-      if (need_mask) {
+      if (__builtin_expect(need_mask, 0)) {   // rare: its code out of line
         asm volatile("" ::: "memory");
         int lim = N - kbase - 4 * hh;
         if constexpr (CAUSAL) {
@@ -609,7 +609,7 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
           float pv[16], ds[16];
-          if (need_mask) {
+          if (__builtin_expect(need_mask, 0)) {   // rare: its code out of line
             asm volatile("" ::: "memory");
             const int hi = N - qbase - 4 * hh;                                          // rel < hi
             const int lo = CAUSAL ? k0w + 32 * b + l32 - qbase - 4 * hh : -(1 << 30);   // rel >= lo
