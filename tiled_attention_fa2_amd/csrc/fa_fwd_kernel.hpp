@@ -1043,12 +1043,16 @@ fa_fwd_dma_kernel(FwdArgs p) {
             s[b][r] = rel < lim ? s[b][r] : masked_raw;
           }
       }
-      // row max of the raw scores; a tile where no row's max exceeds the
-      // reference by more than tau takes p against the reference as it stands
-      const float ext = swap_halves_max(max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; }));
+      // the lane's max of its raw scores; a tile where no row's max exceeds
+      // the reference by more than tau takes p against the reference as it
+      // stands. Both halves of a row hold its threshold, so the test needs no
+      // exchange: the row max (the two halves combined) is formed only when
+      // the reference moves.
+      const float lane_ext = max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; });
       float alpha = 1.0f;
-      if (__builtin_expect(__any(ext > thr), 0)) {
+      if (__builtin_expect(__any(lane_ext > thr), 0)) {
         // a new exact reference for every row of the wave, O rescaled to it
+        const float ext = swap_halves_max(lane_ext);
         const float m_new = vmax(m_ref, ext * c);
         // a causal chunk can start above a row's diagonal: until the row meets
         // a valid key its reference stays -inf, and a zero subtrahend keeps
