@@ -1049,7 +1049,6 @@ fa_fwd_dma_kernel(FwdArgs p) {
       // exchange: the row max (the two halves combined) is formed only when
       // the reference moves.
       const float lane_ext = max_reduce<NB * 16>([&](int i) { return s[i >> 4][i & 15]; });
-      float alpha = 1.0f;
       if (__builtin_expect(__any(lane_ext > thr), 0)) {
         // a new exact reference for every row of the wave, O rescaled to it
         const float ext = swap_halves_max(lane_ext);
@@ -1058,7 +1057,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
         // a valid key its reference stays -inf, and a zero subtrahend keeps
         // p = 0 and alpha = 0
         const float m_use = m_new == -__builtin_inff() ? 0.0f : m_new;
-        alpha = __builtin_amdgcn_exp2f(m_ref - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_use);
         m_ref = m_new;
         m_sub = m_use - kPBias;
         thr = m_new == -__builtin_inff() ? -__builtin_inff() : (m_use + kTau) * inv_c;
@@ -1066,6 +1065,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[mb][r] *= alpha;
+        l_run *= alpha;
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -1074,7 +1074,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
       float ps[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
       for (int i = 4; i < NB * 16; ++i) ps[i & 3] += s[i >> 4][i & 15];
-      l_run = alpha * l_run + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       Op pop[PV_STEPS];
 #pragma unroll
       for (int n = 0; n < PV_STEPS; ++n) {
