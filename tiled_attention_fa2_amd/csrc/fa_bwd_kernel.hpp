@@ -179,17 +179,21 @@ __device__ __forceinline__ void pipeline_reads() {
 }
 
 // One 32-row tile of a [N][D] bf16 head (rows from r_first; rows >= N read as
-// zero) into LDS at `lds` by DMA: every wave issues NINSTR instructions.
+// zero) into LDS at `lds` by DMA: every wave issues NINSTR instructions under
+// one descriptor, instruction t at the lane offsets goff + t T_ROWS ROW.
 template <int D>
 __device__ __forceinline__ void dma_tile(const unsigned char* head, int N, int r_first, uint32_t lds,
                                          int wave, uint32_t goff) {
   using S = Shape<D>;
+  const int rem = N - r_first;
+  const i32x4_t r = dma_rsrc(head + (size_t)(rem > 0 ? r_first : N) * S::ROW, rem > 0 ? (uint32_t)rem * S::ROW : 0u);
 #pragma unroll
   for (int t = 0; t < S::NINSTR; ++t) {
-    const int r0 = r_first + t * S::T_ROWS;
-    const int rem = N - r0;
-    const uint32_t bytes = rem > 0 ? (uint32_t)rem * S::ROW : 0u;
-    lds_dma16(head + (size_t)(r0 > N ? N : r0) * S::ROW, bytes, lds + 1024 * (wave + kNWaves * t), goff);
+    const uint32_t l = lds + 1024 * (wave + kNWaves * t);
+    if (t == 0)
+      lds_dma16_rsrc<4>(r, l, goff);
+    else
+      lds_dma16_rsrc<0>(r, l, goff + (uint32_t)(t * S::T_ROWS * S::ROW));
   }
 }
 

@@ -704,30 +704,48 @@ __device__ __forceinline__ int swz_v(int row) {
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// One LDS DMA instruction: lane L's 16 bytes at byte voff of the buffer
-// [base, base + bytes) (zeros past its end) land at LDS address lds + 16 L.
-// Written as inline asm on purpose: the compiler tracks a buffer_load ... lds
-// it emits itself as an LDS write and, unable to tell the stages of the ring
-// apart, waits for every DMA in flight (vmcnt(0)) before the next LDS read,
-// i.e. for the prefetch of a later tile before the current one is used. Hidden
-// from it, the DMAs are ordered only by the kernel's own wait_vmcnt + barrier
-// (extra VMEM operations the compiler does not know of can only make its own
-// vmcnt waits stricter). base, bytes and lds must be wave-uniform. The s_nop
-// covers the SALU M0 write -> LDS DMA and VALU SGPR write -> VMEM read waits.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, uint32_t lds, uint32_t voff) {
+// Buffer descriptor (wave-uniform SGPRs) of the raw bytes [base, base + bytes):
+// loads past its end return zeros.
+__device__ __forceinline__ i32x4_t dma_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;
   i32x4_t r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
   r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
   r[3] = 0x00020000;
+  return r;
+}
+// One LDS DMA instruction: lane L's 16 bytes at byte voff of descriptor r's
+// buffer land at LDS address lds + 16 L (lds wave-uniform).
+// Written as inline asm on purpose: the compiler tracks a buffer_load ... lds
+// it emits itself as an LDS write and, unable to tell the stages of the ring
+// apart, waits for every DMA in flight (vmcnt(0)) before the next LDS read,
+// i.e. for the prefetch of a later tile before the current one is used. Hidden
+// from it, the DMAs are ordered only by the kernel's own wait_vmcnt + barrier
+// (extra VMEM operations the compiler does not know of can only make its own
+// vmcnt waits stricter). The M0 write needs one wait state before the DMA;
+// NOP = 4 gives the five a VMEM read needs after a VALU write of r's SGPRs
+// (the readfirstlanes of dma_rsrc), for the first use of a fresh descriptor.
+template <int NOP>
+__device__ __forceinline__ void lds_dma16_rsrc(const i32x4_t& r, uint32_t lds, uint32_t voff) {
+  static_assert(NOP == 0 || NOP == 4, "s_nop 0 or 4");
   const int m0 = __builtin_amdgcn_readfirstlane((int)lds);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(r)
-               : "memory", "m0");
+  if constexpr (NOP == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+// The same with a descriptor of its own for [base, base + bytes).
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, uint32_t lds, uint32_t voff) {
+  lds_dma16_rsrc<4>(dma_rsrc(base, bytes), lds, voff);
 }
 // The same with 4 bytes per lane: lane L's dword at byte voff lands at LDS
 // address lds + 4 L (a dword past the end of the buffer reads as zero).
@@ -776,7 +794,7 @@ fa_fwd_dma_kernel(FwdArgs p) {
   static_assert(D == 128 || (D == 64 && !MX), "head dim 128, or 64 without per-block scales");
   using Op = Operand<DT>;
   constexpr int ES = Traits<DT>::ES, KPL = Traits<DT>::KPL;
-  constexpr int NT = 64 * NWAVES, BM = 32 * NWAVES;
+  constexpr int BM = 32 * NWAVES;
   constexpr int NB = BN / 32, QK_STEPS = D / (2 * KPL), PV_STEPS = BN / (2 * KPL), MB = D / 32;
   constexpr int ROW = D * ES, CPR = ROW / 16;
   constexpr int TILE = BN * ROW;                 // bytes of one K or V tile
@@ -788,7 +806,6 @@ fa_fwd_dma_kernel(FwdArgs p) {
                 "per-block scales: fp8, two stages, one 64-lane dword DMA per scale tile");
   constexpr int STAGE = 2 * TILE + SC_K + SC_V;  // K tile, V tile, then the scales
   constexpr int NINSTR = TILE / 1024 / NWAVES;   // 1 KB DMA instructions per wave per tile
-  constexpr int ROWS_PER_INSTR = 64 / CPR;
   static_assert(TILE % (1024 * NWAVES) == 0, "tile must split into whole DMA instructions");
   static_assert(CPR >= 4, "swizzles need at least 4 chunks per row");
 
@@ -884,8 +901,8 @@ fa_fwd_dma_kernel(FwdArgs p) {
   // ---- DMA: instruction t of this wave fills LDS chunks 64 (wave + NWAVES t) + lane ----
   // row r = chunk / CPR, physical column chunk pc -> logical pc ^ f(r); rows of
   // instruction t are those of t = 0 plus 64 NWAVES t / CPR (a multiple of 8, so
-  // f is unchanged): one per-lane offset serves every t, and the per-tile, per-t
-  // buffer descriptor carries the rest.
+  // f is unchanged): instruction t reads at the lane offsets of t = 0 plus
+  // t T_ROWS ROW bytes, under one descriptor per tile.
   const int dma_row = (64 * wave + lane) / CPR;
   const int dma_pc = lane % CPR;
   const uint32_t k_goff = (uint32_t)dma_row * ROW + 16 * (dma_pc ^ swz_k<DT, D>(dma_row));
@@ -893,18 +910,32 @@ fa_fwd_dma_kernel(FwdArgs p) {
   constexpr int T_ROWS = 64 * NWAVES / CPR;      // rows between instruction t and t+1
   static_assert(T_ROWS % 16 == 0, "swizzle period");
 
+  // one descriptor per tile for K and one for V (base at the tile's first
+  // row, range up to the end of the head: rows >= N read as zero); the
+  // tile's instructions t differ only in their lane offsets t T_ROWS ROW
+  uint32_t k_goff_t[NINSTR], v_goff_t[NINSTR];
+#pragma unroll
+  for (int t = 0; t < NINSTR; ++t) {
+    k_goff_t[t] = k_goff + (uint32_t)(t * T_ROWS * ROW);
+    v_goff_t[t] = v_goff + (uint32_t)(t * T_ROWS * ROW);
+  }
   auto issue_tile = [&](int jt, int buf) {
     const int kbase = jt * BN;
     unsigned char* st = smem + buf * STAGE;
+    const uint32_t bytes = (uint32_t)(N - kbase) * ROW;     // kbase < N for every tile issued
+    const i32x4_t rk = dma_rsrc(Kg + (size_t)kbase * ROW, bytes);
+    const i32x4_t rv = dma_rsrc(Vg + (size_t)kbase * ROW, bytes);
 #pragma unroll
     for (int t = 0; t < NINSTR; ++t) {
-      const int r0 = kbase + t * T_ROWS;
-      const int rem_rows = N - r0;
-      const uint32_t bytes = rem_rows > 0 ? (uint32_t)rem_rows * ROW : 0u;
-      const size_t g0 = (size_t)(r0 > N ? N : r0) * ROW;
       const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_ptr)(st + 1024 * (wave + NWAVES * t));
-      lds_dma16(Kg + g0, bytes, lds, k_goff);
-      lds_dma16(Vg + g0, bytes, lds + TILE, v_goff);
+      // the first use of each descriptor waits out a VALU write of its SGPRs
+      if (t == 0) {
+        lds_dma16_rsrc<4>(rk, lds, k_goff_t[0]);
+        lds_dma16_rsrc<4>(rv, lds + TILE, v_goff_t[0]);
+      } else {
+        lds_dma16_rsrc<0>(rk, lds, k_goff_t[t]);
+        lds_dma16_rsrc<0>(rv, lds + TILE, v_goff_t[t]);
+      }
     }
     if constexpr (MX) {
       if (wave == 0) {
