@@ -178,6 +178,32 @@ __device__ __forceinline__ void pipeline_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, LOOK * M, 0);
 }
 
+// S and dP of the dK/dV kernel as inline-asm MFMAs, so that their
+// accumulators are VGPRs. The compiler gives all MFMAs of a kernel one register
+// class; with the dK/dV accumulators taking every AGPR it chose AGPRs for S and
+// dP as well, then copied them out for the softmax and moved dK/dV accumulators
+// to VGPRs and back to make room, every tile. Hidden in asm, these MFMAs carry
+// their own wait states: two before (a VALU write of an operand, e.g. a copy
+// the compiler adds) and drain_vacc() before the VALU reads the results.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_vacc(const Operand<kBF16>& a, const Operand<kBF16>& b, f32x16& c) {
+  const u32x4 av = {a.w[0], a.w[1], a.w[2], a.w[3]};
+  const u32x4 bv = {b.w[0], b.w[1], b.w[2], b.w[3]};
+  if constexpr (FIRST)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(av), "v"(bv));
+  else
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+}
+// 16 wait states: an 8-pass MFMA's result is readable by the VALU after 11.
+template <int KB>
+__device__ __forceinline__ void drain_vacc(f32x16 (&s)[KB], f32x16 (&dp)[KB]) {
+  static_assert(KB == 1 || KB == 2, "one or two key blocks");
+  if constexpr (KB == 1)
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(dp[0]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]), "+v"(dp[0]), "+v"(dp[1]));
+}
+
 // One 32-row tile of a [N][D] bf16 head (rows from r_first; rows >= N read as
 // zero) into LDS at `lds` by DMA: every wave issues NINSTR instructions under
 // one descriptor, instruction t at the lane offsets goff + t T_ROWS ROW.
@@ -434,13 +460,16 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_merge_kernel(BwdArgs p) {
 // dK, dV: one workgroup per (batch * key/value head, 128 KB keys); each wave
 // owns KB blocks of 32 keys and loops over the query tiles of every query head
 // of its group. The kernel waits on its LDS reads: at one wave per SIMD with
-// every register taken, one operand pair is in flight at a time and each pair
-// of MFMAs waits for the reads before it. With KB = 2 every Q / dO operand
-// read, row-major or transposed, feeds the MFMAs of both key blocks, which
-// halves the read-and-wait rounds per flop. The K and V operands of
+// every register taken, nothing else hides a read's latency, so every MFMA
+// phase reads its operands two steps ahead of the MFMAs that use them, and
+// with KB = 2 every Q / dO operand read, row-major or transposed, feeds the
+// MFMAs of both key blocks, which halves the read-and-wait rounds per flop. The K and V operands of
 // blocks b < KREG stay in registers; those of the others (when registers do not
 // suffice) in LDS, lane-major per operand, each lane reading back only what it
 // wrote (16 cheap row-major reads per tile and block, no bank conflicts).
+// The dK/dV accumulators (KB = 2: all 256 AGPRs) are the only MFMA
+// accumulators in AGPRs: S and dP come from asm MFMAs into VGPRs (mfma_vacc),
+// where the softmax reads them without copies.
 #ifndef FA_DKDV_LOOK
 #define FA_DKDV_LOOK 2
 #endif
@@ -555,44 +584,48 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
       if (wave_active) {
         const unsigned char* st = smem + buf * STAGE;
         f32x16 s[KB], dp[KB];
+        // the operands of step kk: Q and dO rows, and the K, V operands of the
+        // blocks staged in LDS; read kDkdvLook steps ahead of their MFMAs (the
+        // scheduler's MFMA groups do not see asm, so the order is written out,
+        // one scheduling fence per step)
+        constexpr int NL = KB - KREG > 0 ? KB - KREG : 1;
+        struct StepOps { Op a, bo, kl[NL], vl[NL]; };
+        StepOps ops[kDkdvLook + 1];
+        auto load_step = [&](int kk, StepOps& o) {
+          bwd::read_rm<D>(st, rb, kk, o.a);
+          bwd::read_rm<D>(st + TILE, rb, kk, o.bo);
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+          for (int b = KREG; b < KB; ++b) {
+            const u32x4 x = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + kk) * 1024 + 16 * lane);
+            const u32x4 y = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + QK + kk) * 1024 + 16 * lane);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            s[b][r] = 0.0f;
-            dp[b][r] = 0.0f;
+            for (int w = 0; w < 4; ++w) {
+              o.kl[b - KREG].w[w] = x[w];
+              o.vl[b - KREG].w[w] = y[w];
+            }
           }
+        };
+#pragma unroll
+        for (int kk = 0; kk < kDkdvLook; ++kk) load_step(kk, ops[kk]);
 #pragma unroll
         for (int kk = 0; kk < QK; ++kk) {
-          Op a, bo;
-          bwd::read_rm<D>(st, rb, kk, a);
+          const StepOps& o = ops[kk % (kDkdvLook + 1)];
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
-            if (b < KREG) {
-              mfma<kBF16>(a, kop[b < KREG ? b : 0][kk], s[b]);
-            } else {
-              Op kl;
-              const u32x4 x = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + kk) * 1024 + 16 * lane);
-#pragma unroll
-              for (int w = 0; w < 4; ++w) kl.w[w] = x[w];
-              mfma<kBF16>(a, kl, s[b]);
-            }
+            const Op& kb_op = b < KREG ? kop[b < KREG ? b : 0][kk] : o.kl[b >= KREG ? b - KREG : 0];
+            if (kk == 0) bwd::mfma_vacc<true>(o.a, kb_op, s[b]);
+            else bwd::mfma_vacc<false>(o.a, kb_op, s[b]);
           }
-          bwd::read_rm<D>(st + TILE, rb, kk, bo);
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
-            if (b < KREG) {
-              mfma<kBF16>(bo, vop[b < KREG ? b : 0][kk], dp[b]);
-            } else {
-              Op vl;
-              const u32x4 y = *(const u32x4*)(kvl + ((b - KREG) * 2 * QK + QK + kk) * 1024 + 16 * lane);
-#pragma unroll
-              for (int w = 0; w < 4; ++w) vl.w[w] = y[w];
-              mfma<kBF16>(bo, vl, dp[b]);
-            }
+            const Op& vb_op = b < KREG ? vop[b < KREG ? b : 0][kk] : o.vl[b >= KREG ? b - KREG : 0];
+            if (kk == 0) bwd::mfma_vacc<true>(o.bo, vb_op, dp[b]);
+            else bwd::mfma_vacc<false>(o.bo, vb_op, dp[b]);
           }
+          if (kk + kDkdvLook < QK) load_step(kk + kDkdvLook, ops[(kk + kDkdvLook) % (kDkdvLook + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        bwd::pipeline_reads<QK, 2 + 2 * (KB - KREG), 2 * KB, kDkdvLook>();
+        bwd::drain_vacc<KB>(s, dp);
         // (L2, D) of the lane's 16 queries qbase + 8 (r / 4) + 4 hh + r % 4
         float l2[16], dd[16];
         const float* ldt = (const float*)(st + 2 * TILE);
