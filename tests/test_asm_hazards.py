@@ -17,10 +17,11 @@ may intervene (a path from elsewhere could not be checked).
 MFMA (the backward's S and dP products, `v_mfma_f32_32x32x16_bf16` into VGPRs):
 an operand written by a VALU instruction needs two wait states before the
 MFMA reads it (each asm block starts with `s_nop 1`), and the 8-pass result
-is not readable by other instructions for 11 wait states. Walking forward from
+is not readable by other instructions for 12 wait states on gfx950 (what the
+compiler itself leaves after such an MFMA). Walking forward from
 every asm MFMA, nothing but the next MFMA of the same accumulation chain
 (same registers as destination and accumulator input) may touch its
-destination registers within 11 wait states, and no label or branch may
+destination registers within 12 wait states, and no label or branch may
 intervene.
 """
 from __future__ import annotations
@@ -101,7 +102,7 @@ def check_asm(text: str):
     return checked, bad
 
 
-MFMA_WAIT = 11
+MFMA_WAIT = 12
 
 
 def _vgprs(tok: str) -> set[int]:

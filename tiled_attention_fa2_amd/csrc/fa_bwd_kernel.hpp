@@ -194,7 +194,8 @@ __device__ __forceinline__ void mfma_vacc(const Operand<kBF16>& a, const Operand
   else
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
 }
-// 16 wait states: an 8-pass MFMA's result is readable by the VALU after 11.
+// 16 wait states: an 8-pass MFMA's result is readable by other instructions
+// after 12 on gfx950.
 template <int KB>
 __device__ __forceinline__ void drain_vacc(f32x16 (&s)[KB], f32x16 (&dp)[KB]) {
   static_assert(KB == 1 || KB == 2, "one or two key blocks");
