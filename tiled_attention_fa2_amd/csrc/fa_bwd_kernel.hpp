@@ -481,7 +481,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 fa_bwd_dkdv_kernel(BwdArgs p) {
   using S = bwd::Shape<D>;
   using Op = Operand<kBF16>;
-  constexpr int QK = S::QK_STEPS, PV = S::PV_STEPS, MB = S::MB, ROW = S::ROW, TILE = S::TILE;
+  constexpr int QK = S::QK_STEPS, MB = S::MB, ROW = S::ROW, TILE = S::TILE;
+  static_assert(S::PV_STEPS == 2, "two contraction steps over a 32-query tile: the softmax halves");
   constexpr int STAGE = 2 * TILE + 1024;    // Q tile, dO tile, 32 (L2, D) pairs (1 KB slot)
   static_assert(KREG >= 1 && KREG <= KB, "at least one key block in registers");
   constexpr int KVL_WAVE = (KB - KREG) * 2 * QK * 1024;   // staged K, V operands of one wave
@@ -640,38 +641,54 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
           l2[4 * b4 + 2] = x1.x; dd[4 * b4 + 2] = x1.y;
           l2[4 * b4 + 3] = x1.z; dd[4 * b4 + 3] = x1.w;
         }
-        // P = exp2(S c - L2), dS = P (dP - D); query qbase + 4hh + rel is
-        // valid for key block b iff it is < N and (causal) >= the lane's key
+        // P = exp2(S c - L2), dS = P (dP - D), in two halves of the lane's
+        // 16 slots: slots 8h .. 8h + 7 make the operands of contraction step
+        // n = h of the products below, so the products of step 0 need only
+        // half 0 and half 1 can be computed beside them. Query qbase + 4hh +
+        // rel is valid for key block b iff it is < N and (causal) >= the
+        // lane's key; invalid slots are computed like the others, then set to
+        // zero (a masked slot's exp2 may overflow; the select drops it).
         const bool need_mask = (qbase + 32 > N) || (CAUSAL && qbase < k0w + 32 * KB - 1);
         Op pop[KB][2], dsop[KB][2];
+        float pv[KB][8], ds[KB][8];
+        auto soft = [&](int h) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          float pv[16], ds[16];
+          for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 8 * h + i;
+              pv[b][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -l2[r]));
+              ds[b][i] = pv[b][i] * (dp[b][r] - dd[r]);
+            }
+        };
+        auto fix_and_pack = [&](int h) {
           if (__builtin_expect(need_mask, 0)) {   // rare: its code out of line
             asm volatile("" ::: "memory");
-            const int hi = N - qbase - 4 * hh;                                          // rel < hi
-            const int lo = CAUSAL ? k0w + 32 * b + l32 - qbase - 4 * hh : -(1 << 30);   // rel >= lo
+            const int hi = N - qbase - 4 * hh;   // rel < hi
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rel = 8 * (r >> 2) + (r & 3);
-              const float t = (rel < hi && rel >= lo) ? __builtin_fmaf(s[b][r], c, -l2[r]) : -__builtin_inff();
-              pv[r] = __builtin_amdgcn_exp2f(t);
-              ds[r] = pv[r] * (dp[b][r] - dd[r]);
-            }
-          } else {
+            for (int b = 0; b < KB; ++b) {
+              const int lo = CAUSAL ? k0w + 32 * b + l32 - qbase - 4 * hh : -(1 << 30);   // rel >= lo
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -l2[r]));
-              ds[r] = pv[r] * (dp[b][r] - dd[r]);
+              for (int i = 0; i < 8; ++i) {
+                const int r = 8 * h + i;
+                const int rel = 8 * (r >> 2) + (r & 3);
+                const bool ok = rel < hi && rel >= lo;
+                pv[b][i] = ok ? pv[b][i] : 0.0f;
+                ds[b][i] = ok ? ds[b][i] : 0.0f;
+              }
             }
           }
-          bwd::pack_b(pv, pop[b]);
-          bwd::pack_b(ds, dsop[b]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed, once
-        // for all key blocks)
 #pragma unroll
-        for (int n = 0; n < PV; ++n)
+          for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              pop[b][h].w[w] = pack_bf16(pv[b][2 * w], pv[b][2 * w + 1]);
+              dsop[b][h].w[w] = pack_bf16(ds[b][2 * w], ds[b][2 * w + 1]);
+            }
+        };
+        // dV^T += dO^T P and dK^T += Q^T dS for contraction step n (A operands
+        // read transposed, once for all key blocks)
+        auto products = [&](int n) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             Op a, bq;
@@ -682,7 +699,16 @@ fa_bwd_dkdv_kernel(BwdArgs p) {
 #pragma unroll
             for (int b = 0; b < KB; ++b) mfma<kBF16>(bq, dsop[b][n], dk[b][mb]);
           }
-        bwd::pipeline_reads<PV * MB, 4, 2 * KB, kDkdvLook>();
+        };
+        constexpr int LKH = kDkdvLook < MB ? kDkdvLook : MB - 1;   // look-ahead inside a half
+        soft(0);
+        fix_and_pack(0);
+        products(0);
+        soft(1);
+        bwd::pipeline_reads<MB, 4, 2 * KB, LKH>();
+        fix_and_pack(1);
+        products(1);
+        bwd::pipeline_reads<MB, 4, 2 * KB, LKH>();
       }
       wait_vmcnt<0>();
       __syncthreads();
