@@ -111,6 +111,30 @@ def test_backward_stress_inputs():
             _check(q, k, v, do, causal, 1.0 / math.sqrt(128), label=variant)
 
 
+def test_backward_masked_scores_overflow():
+    """Causal rows whose masked (future) keys score far above their own
+    logsumexp: the last 16 keys of the sequence have norms 60x the others, so
+    for the earlier queries exp2(S c - L2) of those masked slots overflows in
+    float32 (checked below on the CPU). The dK/dV kernel computes masked slots
+    like the others and zeroes them afterwards; the gradients must stay finite
+    and match the oracle."""
+    N, d = 300, 128
+    q, k, v = make_qkv(1, 2, N, d, "bf16", seed=11)
+    k = k.clone()
+    k[:, :, N - 16:, :] = (k[:, :, N - 16:, :].float() * 60.0).to(torch.bfloat16)
+    do = make_dout(1, 2, N, d, seed=12)
+    scale = 1.0 / math.sqrt(d)
+    # the overflow happens where the kernel computes masked slots (queries of
+    # the last 64 rows, the diagonal tiles of the last keys): some masked
+    # (query, key) pair has S c - L2 > 128
+    _, L = oracle.attention(q, k, v, scale, causal=True)
+    S = np.einsum("bhqd,bhkd->bhqk", q.double().numpy(), k.double().numpy()) * scale
+    excess = (S - L[..., None]) * math.log2(math.e)
+    future = np.triu(np.ones((N, N), dtype=bool), 1)[N - 64:, N - 16:]
+    assert np.max(excess[:, :, N - 64:, N - 16:][..., future]) > 130.0
+    _check(q, k, v, do, True, scale, label="masked overflow")
+
+
 def test_backward_deterministic():
     q, k, v = (t.cuda() for t in make_qkv(1, 4, 1000, 128, "bf16", seed=9))
     do = make_dout(1, 4, 1000, 128, seed=10).cuda()
