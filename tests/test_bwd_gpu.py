@@ -88,11 +88,12 @@ def test_backward_dq_key_split(d, causal):
     assert all(torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_gqa(causal):
-    q, k, v = make_gqa(1, 8, 2, 400, 128, "bf16", seed=3)
-    do = make_dout(1, 8, 400, 128, seed=4)
-    _check(q, k, v, do, causal, 1.0 / math.sqrt(128), label="gqa 8/2")
+def test_backward_gqa(d, causal):
+    q, k, v = make_gqa(1, 8, 2, 400, d, "bf16", seed=3)
+    do = make_dout(1, 8, 400, d, seed=4)
+    _check(q, k, v, do, causal, 1.0 / math.sqrt(d), label=f"gqa 8/2 d={d}")
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
